@@ -1,0 +1,143 @@
+/*
+ * fuse.h -- C ABI of libfuse: fused GEMM + epilogue and RMSNorm -> Linear
+ * operators for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (page title, section that defines them):
+ *
+ *  fuse_gemm_epilogue
+ *      Y = act(A . W + bias) + residual.
+ *      "llm-fusion-compiler" (JohnScheuer): pattern table (gemm_bias_gelu,
+ *      gemm_bias_silu, gemm_bias_relu, gemm_bias, gemm_bias_residual,
+ *      gemm_gelu, gemm_silu) and the usage example, which builds
+ *      gemm -> bias -> activation on x (M,K), w (K,N), bias (N,).
+ *
+ *  fuse_rmsnorm_gemm
+ *      Y = act(RMSNorm_{gamma,eps}(X) . W + bias), the normalised activation
+ *      never written to memory.
+ *      "LLMBoost" (saitejasrivilli): problem statement (the RMSNorm output is
+ *      written out and read straight back by the next Linear; fusion keeps it
+ *      on chip), section 1 (fused op taking x, the norm weight, the
+ *      projection weight and an epsilon attribute; shapes verified before
+ *      execution), section 3 (per-row rsqrt(sum_sq / d_in + eps)); deplodock
+ *      post, RMSNorm loop nest (mean square, plus eps, rsqrt, times x, times
+ *      weight).
+ *
+ *  fuse_rmsnorm_gemm_swiglu
+ *      H = SiLU(Xhat . Wg) * (Xhat . Wu), Xhat = RMSNorm_{gamma,eps}(X): the
+ *      gate and up projections of a SwiGLU FFN sharing one normalised input
+ *      tile, with the gating product in the epilogue.
+ *      "llm-fusion-compiler": FFN block (SwiGLU style), fused into a
+ *      gemm + SiLU kernel and a gemm + bias + residual kernel; the second
+ *      kernel is fuse_gemm_epilogue(H, Wd, bias, X, FUSE_ACT_NONE).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  Layout      Dense, row-major, contiguous, no strides.  A/X is [M,K], W/Wg/Wu
+ *              is [K,N] (N contiguous), bias is [N], residual and Y are [M,N],
+ *              gamma is [K].
+ *  dtype       FUSE_F16 or FUSE_BF16 gives the type of every input (A/X, W,
+ *              bias, residual, gamma) and, by default, of the output.  OR-ing
+ *              FUSE_OUT_F32 makes the output float32 instead.  Products are
+ *              accumulated in float32; bias, activation, residual and the
+ *              RMSNorm factor are applied in float32; the output is rounded
+ *              once, to nearest even.  In fuse_rmsnorm_gemm the normalised
+ *              operand is rounded to the input dtype before the matrix-core
+ *              multiply.
+ *  Shapes      M >= 0 (M == 0 is a no-op returning FUSE_OK), N >= 8, K >= 8,
+ *              N % 8 == 0, K % 8 == 0; every tensor below 2^31 elements.
+ *  Alignment   Every pointer 16-byte aligned.
+ *  Ownership   All pointers are device memory owned by the caller.  The library
+ *              keeps no pointer after the call returns.
+ *  Stream      `stream` is a hipStream_t (NULL: the default stream).  Calls are
+ *              asynchronous: they return once the kernel is enqueued.
+ *  Aliasing    Y must not overlap any input, except Y == residual exactly
+ *              (in-place residual update, allowed only when the output dtype
+ *              equals the input dtype).
+ *  Errors      Returned as a status code; nothing is printed and no exception
+ *              crosses the ABI.  All argument checks finish before any HIP
+ *              call, so a rejected call has no effect on the device.  Faults
+ *              inside a kernel surface at the caller's next synchronisation.
+ *  Threads     Entry points may be called from several host threads.
+ */
+#ifndef LIBFUSE_FUSE_H
+#define LIBFUSE_FUSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FUSE_ABI_VERSION 1
+
+/* Epilogue activation applied to (accumulator + bias). */
+enum fuse_act {
+    FUSE_ACT_NONE = 0,      /* identity                                        */
+    FUSE_ACT_RELU = 1,      /* max(0, z)                                       */
+    FUSE_ACT_GELU_TANH = 2, /* 0.5 z (1 + tanh(sqrt(2/pi)(z + 0.044715 z^3)))  */
+    FUSE_ACT_SILU = 3       /* z * sigmoid(z)                                  */
+};
+
+/* Element types; FUSE_OUT_F32 is a flag OR-ed onto the input type. */
+enum fuse_dtype {
+    FUSE_F16 = 0,
+    FUSE_BF16 = 1,
+    FUSE_OUT_F32 = 0x100
+};
+
+/* Status codes. */
+enum fuse_status {
+    FUSE_OK = 0,
+    FUSE_E_NULL = 1,  /* a required pointer is NULL                         */
+    FUSE_E_SHAPE = 2, /* M < 0, N or K < 8 or not a multiple of 8, too big   */
+    FUSE_E_ALIGN = 3, /* a pointer is not 16-byte aligned                    */
+    FUSE_E_ENUM = 4,  /* unknown act, dtype or flag                          */
+    FUSE_E_EPS = 5,   /* eps < 0 or not finite                               */
+    FUSE_E_ALIAS = 6, /* output overlaps an input (other than Y == residual) */
+    FUSE_E_HIP = 7    /* the HIP runtime reported an error at launch         */
+};
+
+/*
+ * Y[M,N] = act(A[M,K] . W[K,N] + bias[N]) + residual[M,N]
+ *
+ * A, W, Y required; bias and residual may be NULL (read as zero).  The
+ * residual is added after the activation.  `act` is an enum fuse_act, `dtype`
+ * an enum fuse_dtype value (optionally | FUSE_OUT_F32).
+ */
+int fuse_gemm_epilogue(const void* A, const void* W, const void* bias,
+                       const void* residual, void* Y, int64_t M, int64_t N,
+                       int64_t K, int act, int dtype, void* stream);
+
+/*
+ * Y[M,N] = act(RMSNorm(X)[M,K] . W[K,N] + bias[N])
+ * RMSNorm(X)[m,k] = X[m,k] * gamma[k] / sqrt(mean_k(X[m,k]^2) + eps)
+ *
+ * X, gamma, W, Y required; bias may be NULL.  eps is a float32 >= 0.  The
+ * normalisation runs over K, the GEMM's reduction axis.
+ */
+int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
+                      const void* W, const void* bias, void* Y, int64_t M,
+                      int64_t N, int64_t K, int act, int dtype, void* stream);
+
+/*
+ * H[M,F] = SiLU(Xhat . Wg) * (Xhat . Wu),  Xhat = RMSNorm_{gamma,eps}(X)
+ *
+ * X [M,K], gamma [K], Wg and Wu [K,F], H [M,F]; all required.  F follows the
+ * same rules as N above.
+ */
+int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
+                             const void* Wg, const void* Wu, void* H,
+                             int64_t M, int64_t F, int64_t K, int dtype,
+                             void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fuse_strerror(int status);
+
+/* FUSE_ABI_VERSION of the loaded library. */
+int fuse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFUSE_FUSE_H */
