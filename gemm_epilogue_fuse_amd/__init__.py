@@ -1,0 +1,206 @@
+"""libfuse: fused GEMM + epilogue and RMSNorm -> Linear on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/fuse.h``.  It only checks
+and marshals arguments (dtype, device, contiguity, shapes) and passes raw
+device pointers plus the current HIP stream; every step of the computation
+runs in the HIP kernels of ``libfuse.so``.  PyTorch supplies device memory and
+streams.  There is no fallback: if ``libfuse.so`` is missing or cannot be
+loaded, every call raises.
+
+Build the library with ``python -m gemm_epilogue_fuse_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "gemm_epilogue", "rmsnorm_gemm", "rmsnorm_gemm_swiglu", "swiglu_ffn", "plan_name", "set_plan",
+    "FuseError", "lib", "LIB_PATH", "ACT", "F16", "BF16", "OUT_F32",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfuse.so")
+
+ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
+F16, BF16, OUT_F32 = 0, 1, 0x100
+OP_GEMM, OP_RMS_GEMM, OP_RMS_SWIGLU = 0, 1, 2
+
+_lib = None
+
+
+class FuseError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().fuse_strerror(status).decode()
+        if status == 7:
+            msg += ", hipError_t %d" % lib().fuse_last_hip_error()
+        super().__init__("%s failed: status %d (%s)" % (what, status, msg))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfuse.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfuse.so not found at %s; build it with "
+                               "`python -m gemm_epilogue_fuse_amd.build`" % LIB_PATH)
+        # libfuse must run on the same HIP runtime instance that owns the
+        # caller's memory and streams.  torch's HIP libraries ask for the
+        # runtime by file name while libfuse asks by soname, so torch is loaded
+        # first: libfuse then binds to the runtime already in the process
+        # instead of pulling in a second one.
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.fuse_gemm_epilogue.restype = ci
+        L.fuse_gemm_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.fuse_rmsnorm_gemm.restype = ci
+        L.fuse_rmsnorm_gemm.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.fuse_rmsnorm_gemm_swiglu.restype = ci
+        L.fuse_rmsnorm_gemm_swiglu.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, vp]
+        L.fuse_plan_name.restype = ctypes.c_char_p
+        L.fuse_plan_name.argtypes = [ci, i64, i64, i64, ci]
+        L.fuse_set_plan.restype = ci
+        L.fuse_set_plan.argtypes = [ctypes.c_char_p]
+        L.fuse_strerror.restype = ctypes.c_char_p
+        L.fuse_strerror.argtypes = [ci]
+        L.fuse_version.restype = ci
+        L.fuse_version.argtypes = []
+        L.fuse_last_hip_error.restype = ci
+        L.fuse_last_hip_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, out_dtype) -> int:
+    torch = _torch()
+    if t.device.type != "cuda":
+        raise ValueError("libfuse runs on the GPU only; got a tensor on %s" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("inputs must be contiguous")
+    if t.dtype == torch.float16:
+        code = F16
+    elif t.dtype == torch.bfloat16:
+        code = BF16
+    else:
+        raise TypeError("inputs must be float16 or bfloat16, got %s" % t.dtype)
+    if out_dtype is None or out_dtype == t.dtype:
+        return code
+    if out_dtype == torch.float32:
+        return code | OUT_F32
+    raise TypeError("output dtype must be the input dtype or float32")
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _out(out, shape, dtype, device, name="out"):
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _check(out, name, dtype, shape, device)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _act(act) -> int:
+    if isinstance(act, str):
+        if act not in ACT:
+            raise ValueError("unknown activation %r" % act)
+        return ACT[act]
+    return int(act)
+
+
+def gemm_epilogue(A, W, bias=None, residual=None, act="none", out=None, out_dtype=None):
+    """Y = act(A @ W + bias) + residual in one kernel.
+
+    A [M,K], W [K,N], bias [N], residual [M,N]; fp16 or bf16, contiguous, on one
+    GPU.  ``out_dtype`` may be torch.float32.  ``out`` may be ``residual``
+    (in-place update) when the output dtype is the input dtype.
+    """
+    torch = _torch()
+    M, K = A.shape
+    N = W.shape[1]
+    _check(W, "W", A.dtype, (K, N), A.device)
+    _check(bias, "bias", A.dtype, (N,), A.device)
+    _check(residual, "residual", A.dtype, (M, N), A.device)
+    code = _dtype_code(A, out_dtype)
+    Y = _out(out, (M, N), torch.float32 if code & OUT_F32 else A.dtype, A.device)
+    rc = lib().fuse_gemm_epilogue(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), _ptr(Y),
+                                  M, N, K, _act(act), code, _stream(A.device))
+    if rc != 0:
+        raise FuseError(rc, "fuse_gemm_epilogue")
+    return Y
+
+
+def rmsnorm_gemm(X, gamma, W, eps=1e-6, bias=None, act="none", out=None, out_dtype=None):
+    """Y = act(RMSNorm_{gamma,eps}(X) @ W + bias); the normalised X stays on chip."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[1]
+    _check(gamma, "gamma", X.dtype, (K,), X.device)
+    _check(W, "W", X.dtype, (K, N), X.device)
+    _check(bias, "bias", X.dtype, (N,), X.device)
+    code = _dtype_code(X, out_dtype)
+    Y = _out(out, (M, N), torch.float32 if code & OUT_F32 else X.dtype, X.device)
+    rc = lib().fuse_rmsnorm_gemm(_ptr(X), _ptr(gamma), float(eps), _ptr(W), _ptr(bias), _ptr(Y),
+                                 M, N, K, _act(act), code, _stream(X.device))
+    if rc != 0:
+        raise FuseError(rc, "fuse_rmsnorm_gemm")
+    return Y
+
+
+def rmsnorm_gemm_swiglu(X, gamma, Wg, Wu, eps=1e-6, out=None, out_dtype=None):
+    """H = SiLU(Xhat @ Wg) * (Xhat @ Wu), Xhat = RMSNorm_{gamma,eps}(X), in one kernel."""
+    torch = _torch()
+    M, K = X.shape
+    F = Wg.shape[1]
+    _check(gamma, "gamma", X.dtype, (K,), X.device)
+    _check(Wg, "Wg", X.dtype, (K, F), X.device)
+    _check(Wu, "Wu", X.dtype, (K, F), X.device)
+    code = _dtype_code(X, out_dtype)
+    H = _out(out, (M, F), torch.float32 if code & OUT_F32 else X.dtype, X.device)
+    rc = lib().fuse_rmsnorm_gemm_swiglu(_ptr(X), _ptr(gamma), float(eps), _ptr(Wg), _ptr(Wu), _ptr(H),
+                                        M, F, K, code, _stream(X.device))
+    if rc != 0:
+        raise FuseError(rc, "fuse_rmsnorm_gemm_swiglu")
+    return H
+
+
+def swiglu_ffn(X, gamma, Wg, Wu, Wd, bias_d, eps=1e-6, out_dtype=None, H=None, out=None):
+    """SwiGLU FFN block as two fused kernels: H = rmsnorm_gemm_swiglu(X), Y = H @ Wd + bias_d + X."""
+    H = rmsnorm_gemm_swiglu(X, gamma, Wg, Wu, eps=eps, out=H)
+    return gemm_epilogue(H, Wd, bias_d, X, "none", out=out, out_dtype=out_dtype)
+
+
+def plan_name(op: int, M: int, N: int, K: int, dtype: int = F16) -> str:
+    return lib().fuse_plan_name(op, M, N, K, dtype).decode()
+
+
+def set_plan(name):
+    """Force a single-GEMM tile plan by name (None restores the automatic choice)."""
+    rc = lib().fuse_set_plan(None if name is None else name.encode())
+    if rc != 0:
+        raise FuseError(rc, "fuse_set_plan")

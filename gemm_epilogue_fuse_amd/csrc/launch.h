@@ -1,0 +1,40 @@
+// launch.h -- internal interface between the host entry points (fuse_api.cpp)
+// and the gfx950 kernels (gemm_fused.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lf {
+
+enum class Op : int { GemmEpilogue = 0, RmsGemm = 1, RmsSwiglu = 2 };
+
+// One fused call, already validated.  Pointers are device pointers.
+struct Problem {
+    Op op;
+    const void* A;      // A or X, [M,K]
+    const void* W;      // W or Wg, [K,N]
+    const void* W2;     // Wu for RmsSwiglu, else nullptr
+    const void* bias;   // [N] or nullptr
+    const void* resid;  // [M,N] or nullptr
+    const void* gamma;  // [K] for the RMS ops, else nullptr
+    void* Y;            // [M,N]
+    int64_t M, N, K;
+    float eps;
+    int act;        // enum fuse_act
+    bool bf16;      // input dtype is bf16 (else fp16)
+    bool out_f32;   // output is float32
+};
+
+// Enqueue the kernel(s) for `p` on `stream`.  Returns hipSuccess or the
+// launch error.
+hipError_t launch(const Problem& p, hipStream_t stream);
+
+// Name of the tile configuration `launch` would use for `p` (static string).
+const char* plan_name(const Problem& p);
+
+// Force a single-GEMM plan by name (nullptr or "" = automatic).  Returns
+// false for an unknown name.
+bool set_plan(const char* name);
+
+}  // namespace lf

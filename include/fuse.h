@@ -44,7 +44,7 @@
  *              operand is rounded to the input dtype before the matrix-core
  *              multiply.
  *  Shapes      M >= 0 (M == 0 is a no-op returning FUSE_OK), N >= 8, K >= 8,
- *              N % 8 == 0, K % 8 == 0; every tensor below 2^31 elements.
+ *              N % 8 == 0, K % 8 == 0; every tensor below 2^30 elements.
  *  Alignment   Every pointer 16-byte aligned.
  *  Ownership   All pointers are device memory owned by the caller.  The library
  *              keeps no pointer after the call returns.
@@ -100,7 +100,8 @@ enum fuse_status {
 /*
  * Y[M,N] = act(A[M,K] . W[K,N] + bias[N]) + residual[M,N]
  *
- * A, W, Y required; bias and residual may be NULL (read as zero).  The
+ * A, W, Y required (A, Y and residual may be NULL when M == 0); bias and
+ * residual may be NULL (read as zero).  The
  * residual is added after the activation.  `act` is an enum fuse_act, `dtype`
  * an enum fuse_dtype value (optionally | FUSE_OUT_F32).
  */
@@ -112,7 +113,7 @@ int fuse_gemm_epilogue(const void* A, const void* W, const void* bias,
  * Y[M,N] = act(RMSNorm(X)[M,K] . W[K,N] + bias[N])
  * RMSNorm(X)[m,k] = X[m,k] * gamma[k] / sqrt(mean_k(X[m,k]^2) + eps)
  *
- * X, gamma, W, Y required; bias may be NULL.  eps is a float32 >= 0.  The
+ * X, gamma, W, Y required (X and Y may be NULL when M == 0); bias may be NULL.  eps is a float32 >= 0.  The
  * normalisation runs over K, the GEMM's reduction axis.
  */
 int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
@@ -122,7 +123,8 @@ int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
 /*
  * H[M,F] = SiLU(Xhat . Wg) * (Xhat . Wu),  Xhat = RMSNorm_{gamma,eps}(X)
  *
- * X [M,K], gamma [K], Wg and Wu [K,F], H [M,F]; all required.  F follows the
+ * X [M,K], gamma [K], Wg and Wu [K,F], H [M,F]; all required (X and H may be
+ * NULL when M == 0).  F follows the
  * same rules as N above.
  */
 int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
@@ -130,11 +132,28 @@ int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
                              int64_t M, int64_t F, int64_t K, int dtype,
                              void* stream);
 
+/*
+ * Tile plans.  Each entry point picks a kernel configuration ("plan") from the
+ * problem shape.  fuse_plan_name reports the plan a call with these arguments
+ * would use (op: 0 = fuse_gemm_epilogue, 1 = fuse_rmsnorm_gemm,
+ * 2 = fuse_rmsnorm_gemm_swiglu); it returns "invalid" for an unknown op.
+ * fuse_set_plan forces one plan by name for every later single-GEMM call of
+ * this process (tuning and testing only; NULL or "" restores the automatic
+ * choice) and returns FUSE_E_ENUM for an unknown name.  The override is
+ * process-wide; calls racing with it see either the old or the new plan.
+ */
+const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype);
+int fuse_set_plan(const char* name);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fuse_strerror(int status);
 
 /* FUSE_ABI_VERSION of the loaded library. */
 int fuse_version(void);
+
+/* The hipError_t behind the most recent FUSE_E_HIP returned on the calling
+ * thread (0 if none). */
+int fuse_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,154 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol
+that include/fuse.h declares, and rejects every malformed call with the
+documented status before touching HIP (so no kernel launch happens here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import gemm_epilogue_fuse_amd as lf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fuse.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_EPS, E_ALIAS, E_HIP = range(8)
+
+# Fake, well-aligned device addresses far apart: validation never dereferences
+# them, and every call below fails validation (or is the M == 0 no-op), so no
+# HIP call is made.
+A_, W_, B_, R_, Y_, G_, W2_ = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(7))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fuse_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lf.LIB_PATH):
+        from gemm_epilogue_fuse_amd import build
+        build.build()
+    return lf.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert {"fuse_gemm_epilogue", "fuse_rmsnorm_gemm", "fuse_rmsnorm_gemm_swiglu", "fuse_strerror",
+            "fuse_version", "fuse_plan_name", "fuse_set_plan"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strerror(L):
+    assert L.fuse_version() == 1
+    for code in range(8):
+        s = L.fuse_strerror(code)
+        assert s and s != b"unknown status"
+    assert L.fuse_strerror(99) == b"unknown status"
+
+
+def gemm(L, A=A_, W=W_, bias=None, res=None, Y=Y_, M=64, N=64, K=64, act=0, dtype=0):
+    return L.fuse_gemm_epilogue(A, W, bias, res, Y, M, N, K, act, dtype, None)
+
+
+def rms(L, X=A_, g=G_, eps=1e-6, W=W_, bias=None, Y=Y_, M=64, N=64, K=64, act=0, dtype=0):
+    return L.fuse_rmsnorm_gemm(X, g, eps, W, bias, Y, M, N, K, act, dtype, None)
+
+
+def swiglu(L, X=A_, g=G_, eps=1e-6, Wg=W_, Wu=W2_, H=Y_, M=64, F=64, K=64, dtype=0):
+    return L.fuse_rmsnorm_gemm_swiglu(X, g, eps, Wg, Wu, H, M, F, K, dtype, None)
+
+
+def test_null_pointers(L):
+    assert gemm(L, A=None) == E_NULL
+    assert gemm(L, W=None) == E_NULL
+    assert gemm(L, Y=None) == E_NULL
+    assert rms(L, g=None) == E_NULL
+    assert swiglu(L, Wu=None) == E_NULL
+
+
+@pytest.mark.parametrize("M,N,K", [(-1, 64, 64), (4, 0, 64), (4, 4, 64), (4, 12, 64), (4, 64, 12),
+                                   (4, 64, 0), (1 << 20, 64, 1 << 12), (4, 1 << 31, 8)])
+def test_bad_shapes(L, M, N, K):
+    assert gemm(L, M=M, N=N, K=K) == E_SHAPE
+    assert rms(L, M=M, N=N, K=K) == E_SHAPE
+    assert swiglu(L, M=M, F=N, K=K) == E_SHAPE
+
+
+def test_zero_rows_is_a_noop(L):
+    assert gemm(L, M=0) == OK
+    assert rms(L, M=0) == OK
+    assert swiglu(L, M=0) == OK
+    # empty row operands may be NULL (an empty tensor has no storage) ...
+    assert gemm(L, A=None, Y=None, M=0) == OK
+    assert rms(L, X=None, Y=None, M=0) == OK
+    assert swiglu(L, X=None, H=None, M=0) == OK
+    # ... the weights may not
+    assert gemm(L, W=None, M=0) == E_NULL
+    assert rms(L, g=None, M=0) == E_NULL
+
+
+def test_alignment(L):
+    assert gemm(L, A=A_ + 8) == E_ALIGN
+    assert gemm(L, bias=B_ + 2) == E_ALIGN
+    assert gemm(L, res=R_ + 4) == E_ALIGN
+    assert rms(L, g=G_ + 2) == E_ALIGN
+    assert swiglu(L, H=Y_ + 8) == E_ALIGN
+
+
+def test_enums(L):
+    assert gemm(L, act=4) == E_ENUM
+    assert gemm(L, act=-1) == E_ENUM
+    assert gemm(L, dtype=2) == E_ENUM
+    assert gemm(L, dtype=0x200) == E_ENUM
+    assert rms(L, act=7) == E_ENUM
+    assert swiglu(L, dtype=5) == E_ENUM
+
+
+def test_eps(L):
+    for bad in (-1e-6, math.inf, math.nan):
+        assert rms(L, eps=bad) == E_EPS
+        assert swiglu(L, eps=bad) == E_EPS
+
+
+def test_aliasing(L):
+    # Y overlapping A / W / bias / gamma is rejected
+    assert gemm(L, Y=A_ + 64) == E_ALIAS
+    assert gemm(L, Y=W_) == E_ALIAS
+    assert gemm(L, bias=Y_ + 16) == E_ALIAS
+    assert rms(L, Y=G_) == E_ALIAS
+    assert swiglu(L, H=W2_ + 1024) == E_ALIAS
+    # Y == residual is the one allowed overlap, only with a 16-bit output;
+    # a partial overlap is rejected.  (Checked with M == 0 would skip the
+    # checks, so use the allowed case only through its rejection twin.)
+    assert gemm(L, res=Y_ + 16) == E_ALIAS
+    assert gemm(L, res=Y_, dtype=0x100) == E_ALIAS
+
+
+def test_plans(L):
+    assert lf.plan_name(0, 4096, 4096, 4096) == "256x256x64_w2x2"
+    assert lf.plan_name(1, 512, 4096, 4096) == "128x128x64_w2x2"
+    assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dual_256x128x64_w2x2"
+    assert L.fuse_plan_name(9, 1, 8, 8, 0) == b"invalid"
+    with pytest.raises(lf.FuseError):
+        lf.set_plan("no_such_plan")
+    lf.set_plan("256x256x64_w2x2")
+    try:
+        assert lf.plan_name(1, 64, 64, 64) == "256x256x64_w2x2"
+    finally:
+        lf.set_plan(None)
+    assert lf.plan_name(1, 64, 64, 64) == "128x128x64_w2x2"
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    # host tensors are refused outright: there is no CPU path
+    with pytest.raises(ValueError):
+        lf.gemm_epilogue(torch.zeros(4, 8, dtype=torch.float16), torch.zeros(8, 8, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        lf.rmsnorm_gemm(torch.zeros(4, 8, dtype=torch.bfloat16), torch.ones(8, dtype=torch.bfloat16),
+                        torch.zeros(8, 8, dtype=torch.bfloat16))
