@@ -1,0 +1,268 @@
+// common.h -- device-side building blocks shared by the gfx950 kernels:
+// element conversions, matrix-core wrappers, buffer loads, LDS swizzles, the
+// epilogue activations, the XCD-aware tile order and the LDS-staged epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace lf {
+namespace dev {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset that reads as zero
+
+struct KArgs {
+    const uint16_t* A;
+    const uint16_t* W;
+    const uint16_t* W2;
+    const uint16_t* bias;
+    const uint16_t* resid;
+    const uint16_t* gamma;
+    void* Y;
+    int M, N, K;
+    int tiles_m, tiles_n, group_m;
+    int act;
+    int out_f32;
+    float eps;
+};
+
+// ---------------------------------------------------------------- elements
+
+template <bool BF>
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+    if constexpr (BF) return __uint_as_float(w << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <bool BF>
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+    if constexpr (BF) return __uint_as_float(w & 0xffff0000u);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+template <bool BF>
+__device__ __forceinline__ float h_f32(uint16_t h) {
+    if constexpr (BF) return __uint_as_float((uint32_t)h << 16);
+    else return (float)__builtin_bit_cast(_Float16, h);
+}
+// Round to the 16-bit type, nearest-even.
+template <bool BF>
+__device__ __forceinline__ uint16_t f32_h(float x) {
+    if constexpr (BF) return __builtin_bit_cast(uint16_t, (__bf16)x);
+    else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <bool BF>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_h<BF>(a) | ((uint32_t)f32_h<BF>(b) << 16);
+}
+
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- memory
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Byte offset for a buffer load, or one past the 2 GiB window when the lane
+// is out of range (the buffer bounds check then returns zero).  Built with
+// integer arithmetic so the compiler keeps the loads branch-free.
+__device__ __forceinline__ uint32_t oob_or(uint32_t off, bool valid) {
+    return off | ((uint32_t)(!valid) << 31);
+}
+
+// Chunk swizzle of an LDS row: conflict-free for 8 or 16 consecutive rows
+// read at the same logical chunk, and for 8 rows 8 apart written at the same
+// logical chunk.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// KB x 8 transpose of 16-bit elements (KB = 4 or 8): in[j] holds row j
+// (8 halves), out[i] holds column i (KB halves in its first KB/2 words).
+template <int KB>
+__device__ __forceinline__ void transpose_k8(const u32x4 (&in)[KB], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int d = 0; d < KB / 2; ++d) {
+            const uint32_t a = in[2 * d][i >> 1];
+            const uint32_t b = in[2 * d + 1][i >> 1];
+            out[i][d] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+    }
+}
+
+// ---------------------------------------------------------------- epilogue math
+
+// exp(x) as 2^(x log2 e) on the hardware exp2 unit.
+__device__ __forceinline__ float exp_fast(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
+}
+// GeLU, tanh form; tanh(u) = 1 - 2 / (exp(2u) + 1) saturates cleanly at +-1.
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
+    const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp_fast(2.0f * u) + 1.0f);
+    return 0.5f * z * (1.0f + t);
+}
+__device__ __forceinline__ float silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + exp_fast(-z));
+}
+template <int ACT>
+__device__ __forceinline__ float apply_act(float z) {
+    if constexpr (ACT == 1) return fmaxf(z, 0.0f);
+    else if constexpr (ACT == 2) return gelu_tanh(z);
+    else if constexpr (ACT == 3) return silu(z);
+    else return z;
+}
+
+// ---------------------------------------------------------------- schedule
+
+// Workgroups are handed to the 8 XCDs round-robin by id.  Give every XCD a
+// contiguous range of logical tiles, and walk logical tiles in groups of
+// `group_m` tile-rows (column-major inside a group), so the workgroups that
+// share an XCD's L2 also share A rows and W columns.
+__device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tiles_n, int group_m,
+                                         int& tm, int& tn) {
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int q = nwg >> 3, r = nwg & 7;
+    const int l = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    const int per_group = group_m * tiles_n;
+    const int g = l / per_group;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int li = l - g * per_group;
+    tm = first_m + li % gm;
+    tn = li / gm;
+}
+
+
+// ---------------------------------------------------------------- epilogue
+
+// Finish and store one BM x BN output tile.  The accumulators go through LDS
+// one 32-row slab of the wave tile at a time (register r of a 32x32 block
+// holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32), are read back with
+// each lane owning 8 consecutive columns of one row, finished in fp32 (RMS
+// factor, bias, activation, residual; SiLU(gate)*up for the dual GEMM),
+// rounded once and written with 16-byte stores.  Each wave uses its own LDS
+// region of kStageFloats floats at `stage`; every thread of the workgroup
+// must call this.
+template <int BM, int BN, int WM, int WN, bool BF, bool RMS, int NB>
+struct TileStore {
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int SROW = TN + 8;   // staged row stride (floats)
+    static constexpr int LPR = TN / 8;    // lanes per staged row
+    static constexpr int RPI = 64 / LPR;  // rows per read-back step
+    static constexpr int kStageFloats = NB * 32 * SROW;
+    static constexpr int kBytes = WM * WN * kStageFloats * 4;
+
+    template <int ACT>
+    static __device__ __forceinline__ void run_act(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
+                                                   const float* rs, int m0, int n0) {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        const int wm = wave / WN, wn = wave % WN;
+        const int M = p.M, N = p.N;
+        float* stg = stage + wave * kStageFloats;
+        const int ec = (lane % LPR) * 8;
+        const int er = lane / LPR;
+        const int gcol = n0 + wn * TN + ec;
+        const bool colok = gcol < N;  // N % 8 == 0: a lane's 8 columns are all in or all out
+        const bool has_res = p.resid != nullptr;
+        float bias8[8];
+        {
+            u32x4 bw = {0u, 0u, 0u, 0u};
+            if (p.bias != nullptr && colok) bw = *reinterpret_cast<const u32x4*>(p.bias + gcol);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bias8[2 * q] = lo_f32<BF>(bw[q]);
+                bias8[2 * q + 1] = hi_f32<BF>(bw[q]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int nbi = 0; nbi < NB; ++nbi)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        stg[nbi * 32 * SROW + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SROW + j * 32 +
+                            (lane & 31)] = acc[nbi][i][j][r];
+            __syncthreads();
+            for (int it = 0; it < 32 / RPI; ++it) {
+                const int rr = it * RPI + er;
+                const int rl = wm * TM + i * 32 + rr;
+                const int grow = m0 + rl;
+                const float4* src = reinterpret_cast<const float4*>(stg + rr * SROW + ec);
+                const float4 v0 = src[0], v1 = src[1];
+                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                const float rsc = RMS ? rs[rl] : 1.0f;
+                if constexpr (NB == 2) {
+                    const float4* srcu = reinterpret_cast<const float4*>(stg + 32 * SROW + rr * SROW + ec);
+                    const float4 u0 = srcu[0], u1 = srcu[1];
+                    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = silu(v[e] * rsc) * (u[e] * rsc);
+                } else {
+                    u32x4 rw = {0u, 0u, 0u, 0u};
+                    if (has_res && grow < M && colok)
+                        rw = *reinterpret_cast<const u32x4*>(p.resid + (size_t)grow * N + gcol);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float z = (RMS ? v[e] * rsc : v[e]) + bias8[e];
+                        z = apply_act<ACT>(z);
+                        if (has_res) z += (e & 1) ? hi_f32<BF>(rw[e >> 1]) : lo_f32<BF>(rw[e >> 1]);
+                        v[e] = z;
+                    }
+                }
+                if (grow < M && colok) {
+                    const size_t o = (size_t)grow * N + gcol;
+                    if (p.out_f32) {
+                        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.Y) + o);
+                        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+                        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+                    } else {
+                        u32x4 ow;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) ow[q] = pack2<BF>(v[2 * q], v[2 * q + 1]);
+                        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.Y) + o) = ow;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    static __device__ __forceinline__ void run(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
+                                               const float* rs, int m0, int n0) {
+        if constexpr (NB == 2) {
+            run_act<0>(p, acc, stage, rs, m0, n0);
+        } else {
+            switch (p.act) {
+            case 1: run_act<1>(p, acc, stage, rs, m0, n0); break;
+            case 2: run_act<2>(p, acc, stage, rs, m0, n0); break;
+            case 3: run_act<3>(p, acc, stage, rs, m0, n0); break;
+            default: run_act<0>(p, acc, stage, rs, m0, n0); break;
+            }
+        }
+    }
+};
+
+}  // namespace dev
+}  // namespace lf

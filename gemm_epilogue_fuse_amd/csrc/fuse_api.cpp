@@ -16,7 +16,9 @@
 
 namespace {
 
-constexpr int64_t kMaxElems = int64_t(1) << 30;  // per tensor (buffer offsets are 32-bit)
+// Per tensor: byte offsets of 16-bit elements, plus a K step and the
+// out-of-range bit, must stay below 2^32 (buffer offsets are 32-bit).
+constexpr int64_t kMaxElems = int64_t(1) << 29;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

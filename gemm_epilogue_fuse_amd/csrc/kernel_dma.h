@@ -1,0 +1,281 @@
+// kernel_dma.h -- LDS-DMA pipeline for the fused GEMM kernels on gfx950.
+//
+// Both operands travel global -> LDS with buffer_load_dwordx4 ... lds: no
+// staging registers, so NS LDS stages (NS-1 K steps of loads in flight) cost
+// only LDS.  A wave's DMA instruction fills 1 KiB of LDS (lane l writes bytes
+// [16 l, 16 l + 16) of it); which global 16-byte chunk each lane fetches is
+// free, so the XOR swizzles below are applied on the global side.
+//
+//   A tile  [BM rows][BK k]   K-contiguous, 16-byte chunk c of row r stored
+//                             at chunk c ^ swz_a(r); fragments for the matrix
+//                             cores are plain ds_read_b128.
+//   W tile  [BK rows][BN n]   N-contiguous as in memory, chunk c of k-row kr
+//                             stored at c ^ 4 (kr % 4); B fragments come from
+//                             ds_read_b64_tr_b16, the gfx950 transposing LDS
+//                             read: within each 16-lane group, lane i gets
+//                             element i%4 of the 8 bytes addressed by lane
+//                             4e + i/4, for e = 0..3.  With lane j of the group
+//                             pointing at k-row (j/4), columns 4(j%4)..+3, lane
+//                             i receives column i at four consecutive k, i.e.
+//                             the K-contiguous operand the matrix core needs.
+//   gamma   [BK]             (RMS only) one 1 KiB slot per stage.
+//
+// Synchronisation per K step: wait until this wave's loads for the step have
+// landed (vmcnt), barrier (every wave's loads landed, every wave done with
+// the stage about to be refilled), issue the loads NS-1 steps ahead, compute.
+// The DMA and transposing reads are issued from inline assembly, so the
+// compiler neither waits for them (it does not know they are in flight) nor
+// reorders memory operations across them; the waits are explicit here.
+//
+// Requires K % BK == 0 (the register-staged kernel covers other K).
+#pragma once
+
+#include "common.h"
+
+namespace lf {
+namespace dev {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer descriptor (gfx9 layout): base, stride 0, num_records bytes.
+__device__ __forceinline__ i32x4 rsrc128(const void* p, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = (int)(uint32_t)b;
+    r[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane, global -> LDS at m0 + 16*lane.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ u32x2 ds_tr16(uint32_t addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int ACH>
+__device__ __forceinline__ int swz_a(int r) {
+    if constexpr (ACH == 8) return (r ^ (r >> 3)) & 7;
+    else return (r >> 2) & 3;
+}
+__device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
+
+// x * gamma, rounded to the 16-bit type (nearest even), and sum x^2 in fp32.
+// (Vector elements are copied to scalars before __builtin_bit_cast: applied
+// to an element subscript directly, clang takes element 0 every time.)
+template <bool BF>
+__device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t xq = x[q];
+        const uint32_t gq = g[q];
+        if constexpr (BF) {
+            const bf16x2 xv = __builtin_bit_cast(bf16x2, xq);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, ss, false);
+            o[q] = pack2<true>(lo_f32<true>(xq) * lo_f32<true>(gq), hi_f32<true>(xq) * hi_f32<true>(gq));
+        } else {
+            const f16x2 xv = __builtin_bit_cast(f16x2, xq);
+            ss = __builtin_amdgcn_fdot2(xv, xv, ss, false);
+            const f16x2 prod = xv * __builtin_bit_cast(f16x2, gq);
+            o[q] = __builtin_bit_cast(uint32_t, prod);
+        }
+    }
+    return o;
+}
+
+template <int BM, int BN, int BK, int NS, int WM, int WN, bool BF, bool RMS, int NB>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_dma_kernel(const KArgs p) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int NW = NT / 64;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int ACH = BK / 8;
+    constexpr int BCH = BN / 8;
+    constexpr int A_BYTES = BM * BK * 2;
+    constexpr int B_BYTES = BK * BN * 2;
+    constexpr int G_OFF = A_BYTES + NB * B_BYTES;
+    constexpr int STAGE = G_OFF + (RMS ? 1024 : 0);
+    constexpr int A_LD = A_BYTES / (NT * 16);
+    constexpr int B_LD = B_BYTES / (NT * 16);
+    constexpr int LPT = A_LD + NB * B_LD + (RMS ? 1 : 0);
+    static_assert(ACH == 4 || ACH == 8, "BK must be 32 or 64");
+    static_assert(BCH >= 16, "BN must be at least 128 for the W swizzle");
+    static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tiles must split into 1 KiB DMA rows");
+    static_assert(BK * 2 <= 1024, "gamma slot");
+    static_assert((NS - 2) * LPT <= 63, "vmcnt range");
+    using Store = TileStore<BM, BN, WM, WN, BF, RMS, NB>;
+    static_assert(Store::kBytes <= NS * STAGE, "epilogue staging must fit in the LDS stages");
+
+    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + BM * 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int tm, tn;
+    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const i32x4 rsA = rsrc128(p.A + (size_t)m0 * K, (uint32_t)((size_t)(M - m0) * K * 2));
+    const uint32_t w_bytes = (uint32_t)(((size_t)K * N - n0) * 2);
+    const i32x4 rsW = rsrc128(p.W + n0, w_bytes);
+    const i32x4 rsW2 = rsrc128((NB == 2 ? p.W2 : p.W) + n0, w_bytes);
+    const i32x4 rsG = rsrc128(RMS ? p.gamma : p.W, RMS ? (uint32_t)K * 2u : 0u);
+
+    // Loop-invariant per-lane global offsets of the DMA rows (bytes).  Rows
+    // past M and columns past N carry the out-of-range bit.
+    uint32_t voffA[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int q = (i * NW + wave) * 64 + lane;
+        const int r = q / ACH, lc = (q % ACH) ^ swz_a<ACH>(q / ACH);
+        voffA[i] = oob_or((uint32_t)(r * K + lc * 8) * 2u, m0 + r < M);
+    }
+    uint32_t voffB[B_LD];
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+        const int q = (i * NW + wave) * 64 + lane;
+        const int kr = q / BCH, lc = (q % BCH) ^ swz_b(q / BCH);
+        voffB[i] = oob_or((uint32_t)(kr * N + lc * 8) * 2u, n0 + lc * 8 < N);
+    }
+    const uint32_t voffG = oob_or((uint32_t)lane * 16u, lane < ACH);
+    const uint32_t lds0 = lds_u32(smem);
+
+    auto issue = [&](int s, int k0) {
+        const uint32_t base = lds0 + (uint32_t)(s * STAGE);
+        const uint32_t sa = (uint32_t)k0 * 2u;
+        const uint32_t sw = (uint32_t)k0 * (uint32_t)N * 2u;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) dma16(rsA, base + (uint32_t)((i * NW + wave) * 1024), voffA[i], sa);
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int i = 0; i < B_LD; ++i)
+                dma16(o ? rsW2 : rsW, base + (uint32_t)(A_BYTES + o * B_BYTES + (i * NW + wave) * 1024), voffB[i],
+                      sw);
+        if constexpr (RMS) dma16(rsG, base + (uint32_t)G_OFF, voffG, sa);
+    };
+
+    f32x16 acc[NB][FM][FN];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.0f;
+    float ss[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ss[i] = 0.0f;
+
+    // Per-lane parts of the fragment addresses that do not depend on the step.
+    int arow[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + (lane & 31);
+    const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);           // k-row within a 16-k step
+    const int bcol = wn * TN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    auto compute = [&](int s) {
+        const char* sb = smem + s * STAGE;
+        const uint32_t bbase = lds0 + (uint32_t)(s * STAGE + A_BYTES);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int lc = 2 * ks + (lane >> 5);
+            u32x4 af[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const u32x4*>(sb + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4));
+            u32x2 b0[NB][FN], b1[NB][FN];
+            const int kr = 16 * ks + bkr;
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = bcol + 32 * j;
+                    const uint32_t addr = bbase + (uint32_t)(o * B_BYTES + kr * (BN * 2) +
+                                                             ((((n >> 3) ^ swz_b(kr))) << 4) + (((n >> 2) & 1) << 3));
+                    b0[o][j] = ds_tr16(addr);
+                    b1[o][j] = ds_tr16(addr + 4 * BN * 2);
+                }
+            // the transposing reads were issued from assembly: wait for them
+            // here, tying their results to the wait so nothing reads them early
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[o][j]), "+v"(b1[o][j]));
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[o][j]), "+v"(b1[o][j]));
+            if constexpr (RMS) {
+                const u32x4 g = *reinterpret_cast<const u32x4*>(sb + G_OFF + (lc << 4));
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[i] = rms_scale<BF>(af[i], g, ss[i]);
+            }
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const u32x4 bfrag = {b0[o][j][0], b0[o][j][1], b1[o][j][0], b1[o][j][1]};
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) acc[o][i][j] = mfma32<BF>(af[i], bfrag, acc[o][i][j]);
+                }
+        }
+    };
+
+    const int nk = K / BK;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s, min(s, nk - 1) * BK);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<(NS - 2) * LPT>();
+        __syncthreads();
+        // Steps past the end of K are never computed; they re-read the last
+        // tile so every address stays inside the tensors.
+        issue((kt + NS - 1) % NS, min(kt + NS - 1, nk - 1) * BK);
+        compute(kt % NS);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    float* rs = reinterpret_cast<float*>(smem + NS * STAGE);
+    if constexpr (RMS) {
+        // lanes l and l+32 hold the two k-halves of row l%32 of each fragment
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const float s = ss[i] + __shfl_xor(ss[i], 32);
+            if (wn == 0 && lane < 32) rs[arow[i]] = 1.0f / sqrtf(s / (float)K + p.eps);
+        }
+        __syncthreads();
+    }
+    Store::run(p, acc, reinterpret_cast<float*>(smem), rs, m0, n0);
+}
+
+}  // namespace dev
+}  // namespace lf

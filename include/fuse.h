@@ -44,7 +44,7 @@
  *              operand is rounded to the input dtype before the matrix-core
  *              multiply.
  *  Shapes      M >= 0 (M == 0 is a no-op returning FUSE_OK), N >= 8, K >= 8,
- *              N % 8 == 0, K % 8 == 0; every tensor below 2^30 elements.
+ *              N % 8 == 0, K % 8 == 0; every tensor below 2^29 elements.
  *  Alignment   Every pointer 16-byte aligned.
  *  Ownership   All pointers are device memory owned by the caller.  The library
  *              keeps no pointer after the call returns.

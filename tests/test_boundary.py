@@ -130,18 +130,23 @@ def test_aliasing(L):
 
 
 def test_plans(L):
-    assert lf.plan_name(0, 4096, 4096, 4096) == "256x256x64_w2x2"
-    assert lf.plan_name(1, 512, 4096, 4096) == "128x128x64_w2x2"
-    assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dual_256x128x64_w2x2"
+    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4"
+    assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
+    assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
+    assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"
     assert L.fuse_plan_name(9, 1, 8, 8, 0) == b"invalid"
     with pytest.raises(lf.FuseError):
         lf.set_plan("no_such_plan")
-    lf.set_plan("256x256x64_w2x2")
+    lf.set_plan("dma_256x256x32_s4")
     try:
-        assert lf.plan_name(1, 64, 64, 64) == "256x256x64_w2x2"
+        assert lf.plan_name(1, 64, 64, 64) == "dma_256x256x32_s4"
+        # a forced plan that cannot run the shape is not used
+        assert lf.plan_name(1, 64, 64, 72) == "reg_128x128x64"
+        assert lf.plan_name(2, 64, 128, 64) == "dma_dual_256x128x32_s4"
     finally:
         lf.set_plan(None)
-    assert lf.plan_name(1, 64, 64, 64) == "128x128x64_w2x2"
+    assert lf.plan_name(1, 64, 64, 64) == "dma_128x128x64_s4"
 
 
 def test_python_binding_rejects_bad_tensors():

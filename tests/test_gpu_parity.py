@@ -21,7 +21,12 @@ from parity_util import EPS, EPS32, assert_close, dev_t, sample_rows, say, to64
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["256x256x64_w2x2", "128x128x64_w2x2"]
+PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64"]
+
+
+def fitk(plan, K):
+    """DMA plans need K % 64 == 0: round K up for them (M and N stay ragged)."""
+    return -(-K // 64) * 64 if plan.startswith("dma") else K
 ACTS = ["none", "relu", "gelu_tanh", "silu"]
 
 
@@ -61,7 +66,8 @@ def plan(request):
 @pytest.mark.parametrize("act", ACTS)
 def test_gemm_epilogue_ragged(plan, dtype, act):
     T = torch()
-    M, N, K = 300, 392, 328
+    M, N, K = 300, 392, fitk(plan, 328)
+    assert lf.plan_name(0, M, N, K) == plan
     say("gemm-ragged", plan, dtype, act, M, N, K)
     d = synth.gemm_epilogue_sweep(M, N, K, seed=21, dtype=dtype, residual=True)
     t = {k: dev_t(v, dtype) for k, v in d.items()}
@@ -82,7 +88,8 @@ def test_gemm_epilogue_ragged(plan, dtype, act):
 @pytest.mark.parametrize("act", ACTS)
 def test_rmsnorm_gemm_ragged(plan, dtype, act):
     T = torch()
-    M, D, N = 260, 520, 392
+    M, D, N = 260, fitk(plan, 520), 392
+    assert lf.plan_name(1, M, N, D) == plan
     say("rms-ragged", plan, dtype, act, M, D, N)
     d = synth.rmsnorm_linear(M=M, D=D, N=N, seed=22, dtype=dtype)
     b = synth.to_bits(synth.generator(23).standard_normal(N) * 0.1, dtype)
@@ -102,10 +109,11 @@ def test_rmsnorm_gemm_ragged(plan, dtype, act):
 
 
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
-@pytest.mark.parametrize("M,F,K", [(300, 392, 328), (64, 136, 1000), (513, 264, 72)])
+@pytest.mark.parametrize("M,F,K", [(300, 392, 328), (64, 136, 1000), (513, 264, 72), (300, 392, 320),
+                                   (513, 264, 1024)])
 def test_swiglu_ragged(dtype, M, F, K):
     T = torch()
-    say("swiglu-ragged", dtype, M, F, K)
+    say("swiglu-ragged", dtype, M, F, K, lf.plan_name(2, M, F, K))
     d = synth.swiglu_ffn(M=M, D=K, F=F, seed=24, dtype=dtype)
     t = {k: dev_t(v, dtype) for k, v in d.items()}
     x = w64(d, dtype)

@@ -17,7 +17,12 @@ from parity_util import dev_t, say, to64
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["256x256x64_w2x2", "128x128x64_w2x2"]
+PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64"]
+
+
+def fitk(plan, K):
+    """DMA plans need K % 64 == 0: round K up for them (M and N stay ragged)."""
+    return -(-K // 64) * 64 if plan.startswith("dma") else K
 DTYPES = [synth.F16, synth.BF16]
 ONE = {synth.F16: 0x3C00, synth.BF16: 0x3F80}
 SHAPES = [(1, 8, 8), (7, 24, 40), (65, 136, 72), (129, 264, 200), (300, 392, 328), (520, 776, 264)]
@@ -49,6 +54,8 @@ def nan_filled(shape, dtype):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("M,K", [(1, 8), (7, 40), (65, 136), (300, 328), (513, 264)])
 def test_identity_weight_returns_input(plan, dtype, M, K):
+    K = fitk(plan, K)
+    assert lf.plan_name(0, M, K, K) == plan
     say("identity", plan, dtype, M, K)
     A = rand_bits((M, K), dtype, 100 + M)
     At = dev_t(A, dtype)
@@ -63,6 +70,7 @@ def test_identity_weight_returns_input(plan, dtype, M, K):
 def test_permutation_weights(plan, dtype):
     g = synth.generator(5)
     for M, K in ((33, 24), (260, 136)):
+        K = fitk(plan, K)
         say("perm-cols", plan, dtype, M, K)
         A = rand_bits((M, K), dtype, 200 + M)
         p = g.permutation(K)
@@ -71,6 +79,7 @@ def test_permutation_weights(plan, dtype):
         Y = lf.gemm_epilogue(dev_t(A, dtype), dev_t(P, dtype))
         assert np.array_equal(to64(Y), synth.widen(A, dtype)[:, p])
     for M, N in ((24, 40), (264, 392)):
+        M = fitk(plan, M)  # here M is also the reduction length
         say("perm-rows", plan, dtype, M, N)
         q = g.permutation(M)
         Q = np.zeros((M, M), dtype=np.uint16)
@@ -84,6 +93,8 @@ def test_permutation_weights(plan, dtype):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_integer_data_bit_exact(plan, dtype, M, N, K):
     import torch
+    K = fitk(plan, K)
+    assert lf.plan_name(0, M, N, K) == plan
     say("integer", plan, dtype, M, N, K)
     g = synth.generator(M * 31 + N * 7 + K)
     A = g.integers(-1, 2, (M, K)).astype(np.float64)
@@ -108,6 +119,8 @@ def test_integer_data_bit_exact(plan, dtype, M, N, K):
 def test_rmsnorm_exact_rows(plan, dtype, M, N, K):
     # eps = 0 and rows of +-1 (mean square 1) or +-2 (mean square 4): r = 1 or
     # 1/2 exactly; with W = I the output is sign * gamma bit for bit.
+    K = fitk(plan, K)
+    assert lf.plan_name(1, M, N, K) == plan
     say("rms-exact", plan, dtype, M, N, K)
     g = synth.generator(9 + M)
     sign = g.choice([-1.0, 1.0], size=(M, K))
@@ -129,7 +142,7 @@ def test_rmsnorm_exact_rows(plan, dtype, M, N, K):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_rmsnorm_scale_invariance_random(plan, dtype):
     say("rms-scale", plan, dtype)
-    d = synth.rmsnorm_linear(M=130, D=264, N=136, seed=3, dtype=dtype)
+    d = synth.rmsnorm_linear(M=130, D=fitk(plan, 264), N=136, seed=3, dtype=dtype)
     X = synth.widen(d["X"], dtype)
     # keep x*gamma out of the fp16 subnormal range, where rounding is absolute
     # rather than relative and doubling would not commute with it
@@ -147,6 +160,7 @@ def test_rmsnorm_unit_rms(plan, dtype):
     import torch
     say("rms-unit", plan, dtype)
     M, K = 96, 512
+    assert lf.plan_name(1, M, K, K) == plan
     X = synth.to_bits(synth.generator(4).standard_normal((M, K)), dtype)
     ones = np.full(K, ONE[dtype], dtype=np.uint16)
     Y = lf.rmsnorm_gemm(dev_t(X, dtype), dev_t(ones, dtype), dev_t(eye_bits(K, K, dtype), dtype), eps=1e-6,
@@ -160,11 +174,13 @@ def test_rmsnorm_unit_rms(plan, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_swiglu_plumbing(dtype):
+@pytest.mark.parametrize("K", [264, 320])
+def test_swiglu_plumbing(dtype, K):
     import torch
     # Wg = Wu = I, gamma = 1, rows +-1, eps = 0: H = silu(x) * x exactly per element
-    say("swiglu-plumbing", dtype)
-    M, K = 70, 264
+    # (K = 264 runs the register-staged plan, K = 320 the DMA plan)
+    say("swiglu-plumbing", dtype, K, lf.plan_name(2, 70, K, K))
+    M = 70
     g = synth.generator(11)
     X = g.choice([-1.0, 1.0], size=(M, K))
     I = dev_t(eye_bits(K, K, dtype), dtype)
@@ -199,7 +215,7 @@ def test_deterministic(plan_name):
     lf.set_plan(plan_name)
     try:
         say("determinism", plan_name)
-        d = synth.rmsnorm_linear(M=300, D=520, N=392, seed=1)
+        d = synth.rmsnorm_linear(M=300, D=fitk(plan_name, 520), N=392, seed=1)
         t = {k: dev_t(v, synth.F16) for k, v in d.items()}
         a = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], act="gelu_tanh"))
         b = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], act="gelu_tanh"))
