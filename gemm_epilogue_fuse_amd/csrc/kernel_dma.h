@@ -201,65 +201,129 @@ gemm_dma_kernel(const KArgs p) {
     const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);           // k-row within a 16-k step
     const int bcol = wn * TN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    auto compute = [&](int s) {
-        const char* sb = smem + s * STAGE;
-        const uint32_t bbase = lds0 + (uint32_t)(s * STAGE + A_BYTES);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int lc = 2 * ks + (lane >> 5);
-            u32x4 af[FM];
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(sb + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4));
-            u32x2 b0[NB][FN], b1[NB][FN];
-            const int kr = 16 * ks + bkr;
-#pragma unroll
-            for (int o = 0; o < NB; ++o)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int n = bcol + 32 * j;
-                    const uint32_t addr = bbase + (uint32_t)(o * B_BYTES + kr * (BN * 2) +
-                                                             ((((n >> 3) ^ swz_b(kr))) << 4) + (((n >> 2) & 1) << 3));
-                    b0[o][j] = ds_tr16(addr);
-                    b1[o][j] = ds_tr16(addr + 4 * BN * 2);
-                }
-            // the transposing reads were issued from assembly: wait for them
-            // here, tying their results to the wait so nothing reads them early
-#pragma unroll
-            for (int o = 0; o < NB; ++o)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[o][j]), "+v"(b1[o][j]));
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int o = 0; o < NB; ++o)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(b0[o][j]), "+v"(b1[o][j]));
-            if constexpr (RMS) {
-                const u32x4 g = *reinterpret_cast<const u32x4*>(sb + G_OFF + (lc << 4));
-#pragma unroll
-                for (int i = 0; i < FM; ++i) af[i] = rms_scale<BF>(af[i], g, ss[i]);
-            }
-#pragma unroll
-            for (int o = 0; o < NB; ++o)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const u32x4 bfrag = {b0[o][j][0], b0[o][j][1], b1[o][j][0], b1[o][j][1]};
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) acc[o][i][j] = mfma32<BF>(af[i], bfrag, acc[o][i][j]);
-                }
+    // Fragments of one 16-wide K sub-step, read from LDS by assembly so the
+    // waits below are the only ones: two sets alternate, the reads for
+    // sub-step t+1 (possibly in the next stage) are in flight while the
+    // matrix cores work on sub-step t.
+    struct Frags {
+        u32x4 a[FM];
+        u32x2 b0[NB][FN], b1[NB][FN];
+        u32x4 g;
+    };
+    // One LDS read of the fragments of sub-step ks of stage s: pieces
+    // 0..FM-1 are the A rows, then two transposing reads per (operand,
+    // column block), then gamma.
+    constexpr int NREAD = FM + 2 * NB * FN + (RMS ? 1 : 0);
+    auto read_piece = [&](Frags& f, int s, int ks, int r) {
+        const uint32_t sbase = lds0 + (uint32_t)(s * STAGE);
+        const int lc = 2 * ks + (lane >> 5);
+        if (r < FM) {
+            const int i = r;
+            const uint32_t addr = sbase + (uint32_t)(arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4));
+            asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[i]) : "v"(addr) : "memory");
+        } else if (r < FM + 2 * NB * FN) {
+            const int t = r - FM;
+            const int o = t / (2 * FN), j = (t / 2) % FN, h = t & 1;
+            const int kr = 16 * ks + bkr + 4 * h;
+            const int n = bcol + 32 * j;
+            const uint32_t addr = sbase + (uint32_t)(A_BYTES + o * B_BYTES + kr * (BN * 2) +
+                                                     (((n >> 3) ^ swz_b(kr)) << 4) + (((n >> 2) & 1) << 3));
+            if (h == 0) f.b0[o][j] = ds_tr16(addr);
+            else f.b1[o][j] = ds_tr16(addr);
+        } else {
+            const uint32_t addr = sbase + (uint32_t)(G_OFF + (lc << 4));
+            asm volatile("ds_read_b128 %0, %1" : "=v"(f.g) : "v"(addr) : "memory");
         }
     };
+    // One DMA row of stage s (k offset k0): A rows, then W rows per operand,
+    // then gamma.
+    auto dma_piece = [&](int s, int k0, int d) {
+        const uint32_t base = lds0 + (uint32_t)(s * STAGE);
+        if (d < A_LD) {
+            dma16(rsA, base + (uint32_t)((d * NW + wave) * 1024), voffA[d], (uint32_t)k0 * 2u);
+        } else if (d < A_LD + NB * B_LD) {
+            const int o = (d - A_LD) / B_LD, i = (d - A_LD) % B_LD;
+            dma16(o ? rsW2 : rsW, base + (uint32_t)(A_BYTES + o * B_BYTES + (i * NW + wave) * 1024), voffB[i],
+                  (uint32_t)k0 * (uint32_t)N * 2u);
+        } else {
+            dma16(rsG, base + (uint32_t)G_OFF, voffG, (uint32_t)k0 * 2u);
+        }
+    };
+    // Wait for every outstanding LDS read and tie the fragment registers to
+    // the wait, so nothing consumes them before it.
+    auto wait_frags = [&](Frags& f) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(f.a[i]));
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(f.b0[o][j]), "+v"(f.b1[o][j]));
+        if constexpr (RMS) asm volatile("" : "+v"(f.g));
+    };
 
+    constexpr int KS = BK / 16;
+    constexpr int NMMA = NB * FM * FN;
     const int nk = K / BK;
+    // Prologue: NS-1 stages in flight, wait for the first, queue the next.
+    // Steps past the end of K are never computed; they re-read the last
+    // tile so every address stays inside the tensors.
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, min(s, nk - 1) * BK);
+    wait_vmcnt<(NS - 2) * LPT>();
+    __syncthreads();
+    issue(NS - 1, min(NS - 1, nk - 1) * BK);
+    Frags F0, F1;
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, r);
+    // Sub-step t = kt*KS + ks computes from fragment set t%2.  Its
+    // matrix-core instructions are interleaved one by one with the LDS reads
+    // of sub-step t+1 and, on the first sub-step of a stage, with the DMA of
+    // the stage NS-1 ahead, so neither the LDS queue nor the texture address
+    // FIFOs hold the matrix cores up.  When t+1 opens a new stage this wave
+    // first waits for its own loads of that stage, then a barrier makes every
+    // wave's loads visible and guarantees that no wave still reads the stage
+    // that the DMA is about to refill.
+    auto substep = [&](Frags& cur, Frags& nxt, int kt, int ks) {
+        wait_frags(cur);
+        if constexpr (RMS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) cur.a[i] = rms_scale<BF>(cur.a[i], cur.g, ss[i]);
+        }
+        const bool more_in_stage = ks + 1 < KS;
+        const bool next_stage = !more_in_stage && kt + 1 < nk;
+        if (next_stage) {
+            wait_vmcnt<(NS - 2) * LPT>();
+            __syncthreads();
+        }
+        const int rs_stage = more_in_stage ? kt % NS : (kt + 1) % NS;
+        const int rs_ks = more_in_stage ? ks + 1 : 0;
+        const int k_dma = min(kt + NS, nk - 1) * BK;
+#pragma unroll
+        for (int m = 0; m < NMMA; ++m) {
+            const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
+            const u32x4 bfrag = {cur.b0[o][j][0], cur.b0[o][j][1], cur.b1[o][j][0], cur.b1[o][j][1]};
+            acc[o][i][j] = mfma32<BF>(cur.a[i], bfrag, acc[o][i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < NREAD && (more_in_stage || next_stage)) read_piece(nxt, rs_stage, rs_ks, m);
+            if (m < LPT && next_stage) dma_piece(kt % NS, k_dma, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // reads that did not fit between the matrix-core instructions
+#pragma unroll
+        for (int m = NMMA; m < NREAD; ++m)
+            if (more_in_stage || next_stage) read_piece(nxt, rs_stage, rs_ks, m);
+#pragma unroll
+        for (int m = NMMA; m < LPT; ++m)
+            if (next_stage) dma_piece(kt % NS, k_dma, m);
+    };
+    static_assert(KS % 2 == 0, "sub-steps per stage must be even so the fragment sets line up");
     for (int kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<(NS - 2) * LPT>();
-        __syncthreads();
-        // Steps past the end of K are never computed; they re-read the last
-        // tile so every address stays inside the tensors.
-        issue((kt + NS - 1) % NS, min(kt + NS - 1, nk - 1) * BK);
-        compute(kt % NS);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks += 2) {
+            substep(F0, F1, kt, ks);
+            substep(F1, F0, kt, ks + 1);
+        }
     }
     wait_vmcnt<0>();
     __syncthreads();
