@@ -31,6 +31,12 @@ struct KArgs {
     int act;
     int out_f32;
     float eps;
+    // split-K (DMA kernel only): `splits` workgroups share each output tile,
+    // split z covering K range [z*kchunk, min(K, (z+1)*kchunk)); fp32
+    // partials and per-tile arrival counters live in a library workspace.
+    int splits, kchunk;
+    float* ws;
+    unsigned* cnt;
 };
 
 // ---------------------------------------------------------------- elements
@@ -136,11 +142,14 @@ __device__ __forceinline__ float apply_act(float z) {
 // contiguous range of logical tiles, and walk logical tiles in groups of
 // `group_m` tile-rows (column-major inside a group), so the workgroups that
 // share an XCD's L2 also share A rows and W columns.
-__device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tiles_n, int group_m,
-                                         int& tm, int& tn) {
+__device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tiles_n, int group_m, int splits,
+                                         int& tm, int& tn, int& kz) {
     const int xcd = bid & 7, idx = bid >> 3;
     const int q = nwg >> 3, r = nwg & 7;
-    const int l = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    int l = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    // the splits of one tile are consecutive, hence on the same XCD
+    kz = l % splits;
+    l /= splits;
     const int per_group = group_m * tiles_n;
     const int g = l / per_group;
     const int first_m = g * group_m;
@@ -149,7 +158,6 @@ __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tile
     tm = first_m + li % gm;
     tn = li / gm;
 }
-
 
 // ---------------------------------------------------------------- epilogue
 

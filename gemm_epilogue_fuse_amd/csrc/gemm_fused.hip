@@ -25,7 +25,11 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "kernel_dma.h"
 #include "kernel_reg.h"
@@ -37,25 +41,28 @@ using dev::KArgs;
 
 enum class Kind { Reg, Dma };
 
-// A tile plan: kernel family, tile sizes, K step and LDS stages.
+// A tile plan: kernel family, tile sizes, K step, LDS stages, and whether
+// it can split K across workgroups.
 struct Plan {
     const char* name;
     Kind kind;
     int bm, bn, bk, ns;
     bool dual;
+    bool split;
 };
 
 constexpr Plan kPlans[] = {
-    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, false},
-    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, false},
-    {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, false},
-    {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, false},
-    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, true},
-    {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, true},
+    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, false, false},
+    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, false, true},
+    {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, false, false},
+    {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, false, false},
+    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, true, false},
+    {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, true, false},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
-std::atomic<int> g_override{-1};
+std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
+std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
 
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
@@ -63,13 +70,84 @@ bool plan_fits(const Plan& pl, const Problem& p) {
     return true;
 }
 
-const Plan& choose(const Problem& p) {
+// Workgroups a plan keeps busy at once: the chip has 256 CUs and every
+// tile plan here holds one workgroup per CU.
+constexpr int kCUs = 256;
+
+struct Choice {
+    const Plan* plan;
+    int splits;
+};
+
+// Split K when the output has too few tiles to occupy the CUs: the splits
+// of a tile run on different CUs and are reduced in a fixed order.  Each
+// split keeps at least 8 K steps so the pipeline has room to fill.
+int auto_splits(const Plan& pl, const Problem& p) {
+    if (!pl.split) return 1;
+    const int64_t tiles = ((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn);
+    const int64_t nk = p.K / pl.bk;
+    int s = 1;
+    while (tiles * s * 2 <= kCUs && nk / (s * 2) >= 8) s *= 2;
+    return s;
+}
+
+Choice choose(const Problem& p) {
     const int ov = g_override.load(std::memory_order_relaxed);
-    if (ov >= 0 && plan_fits(kPlans[ov], p)) return kPlans[ov];
-    if (p.op == Op::RmsSwiglu) return (p.K % 32 == 0) ? kPlans[4] : kPlans[5];
-    const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (t256 >= 224) return (p.K % 32 == 0) ? kPlans[0] : kPlans[2];
-    return (p.K % 64 == 0) ? kPlans[1] : kPlans[3];
+    if (ov >= 0 && plan_fits(kPlans[ov], p)) {
+        const int s = g_override_splits.load(std::memory_order_relaxed);
+        const int64_t nk = p.K / kPlans[ov].bk;
+        return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
+    }
+    const Plan* pl;
+    if (p.op == Op::RmsSwiglu) {
+        pl = (p.K % 32 == 0) ? &kPlans[4] : &kPlans[5];
+    } else {
+        const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        if (t256 >= 224) pl = (p.K % 32 == 0) ? &kPlans[0] : &kPlans[2];
+        else pl = (p.K % 64 == 0) ? &kPlans[1] : &kPlans[3];
+    }
+    return {pl, auto_splits(*pl, p)};
+}
+
+// Split-K workspace, one per (device, stream) so calls on different
+// streams never share partials or counters.  Grown on demand; the counters
+// are zeroed once at allocation and every reducing workgroup puts its
+// counter back to zero.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+constexpr size_t kCounterBytes = 1 << 20;  // 256K tiles
+
+hipError_t get_workspace(hipStream_t stream, size_t part_bytes, float** ws, unsigned** cnt) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[{dev, stream}];
+    const size_t need = kCounterBytes + part_bytes;
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // the old buffer may still be in use by queued work on this stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return e;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        const size_t bytes = std::max(need, size_t(64) << 20);
+        e = hipMalloc(&w.ptr, bytes);
+        if (e != hipSuccess) return e;
+        e = hipMemset(w.ptr, 0, kCounterBytes);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) return e;
+        w.bytes = bytes;
+    }
+    *cnt = static_cast<unsigned*>(w.ptr);
+    *ws = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + kCounterBytes);
+    return hipSuccess;
 }
 
 hipError_t launch_fn(const void* fn, const KArgs& a, int nwg, int threads, hipStream_t s) {
@@ -87,11 +165,13 @@ const void* reg_fn(int K) {
 }
 
 template <bool BF, bool RMS>
-const void* single_fn(const Plan& pl, int K) {
+const void* single_fn(const Plan& pl, int K, bool split) {
     if (pl.kind == Kind::Dma) {
         if (pl.bm == 256)
-            return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 256, 32, 4, 2, 2, BF, RMS, 1>);
-        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<128, 128, 64, 4, 2, 2, BF, RMS, 1>);
+            return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 256, 32, 4, 2, 2, BF, RMS, 1, false>);
+        if (split)
+            return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<128, 128, 64, 4, 2, 2, BF, RMS, 1, true>);
+        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<128, 128, 64, 4, 2, 2, BF, RMS, 1, false>);
     }
     if (pl.bm == 256) return reg_fn<256, 256, 2, 2, BF, RMS, 1, 1>(K);
     return reg_fn<128, 128, 2, 2, BF, RMS, 1, 2>(K);
@@ -100,21 +180,41 @@ const void* single_fn(const Plan& pl, int K) {
 template <bool BF>
 const void* dual_fn(const Plan& pl, int K) {
     if (pl.kind == Kind::Dma)
-        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, BF, true, 2>);
+        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, BF, true, 2, false>);
     return reg_fn<256, 128, 2, 2, BF, true, 2, 1>(K);
 }
 
 }  // namespace
 
-const char* plan_name(const Problem& p) { return choose(p).name; }
+const char* plan_name(const Problem& p) {
+    // "<plan>" or "<plan>:k<S>" for S-way split K (static strings)
+    static thread_local char buf[64];
+    const Choice c = choose(p);
+    if (c.splits == 1) return c.plan->name;
+    snprintf(buf, sizeof(buf), "%s:k%d", c.plan->name, c.splits);
+    return buf;
+}
 
 bool set_plan(const char* name) {
     if (name == nullptr || name[0] == 0) {
         g_override.store(-1);
+        g_override_splits.store(0);
         return true;
     }
+    const char* colon = std::strchr(name, ':');
+    const size_t len = colon ? (size_t)(colon - name) : std::strlen(name);
+    int splits = 0;
+    if (colon) {
+        if (colon[1] != 'k') return false;
+        char* end = nullptr;
+        const long v = std::strtol(colon + 2, &end, 10);
+        if (end == colon + 2 || *end != 0 || v < 1 || v > 64) return false;
+        splits = (int)v;
+    }
     for (int i = 0; i < kNumPlans; ++i) {
-        if (std::strcmp(name, kPlans[i].name) == 0) {
+        if (std::strlen(kPlans[i].name) == len && std::strncmp(name, kPlans[i].name, len) == 0) {
+            if (splits > 1 && !kPlans[i].split) return false;
+            g_override_splits.store(splits);
             g_override.store(i);
             return true;
         }
@@ -124,7 +224,8 @@ bool set_plan(const char* name) {
 
 hipError_t launch(const Problem& p, hipStream_t stream) {
     if (p.M == 0) return hipSuccess;
-    const Plan& pl = choose(p);
+    const Choice c = choose(p);
+    const Plan& pl = *c.plan;
     KArgs a;
     a.A = static_cast<const uint16_t*>(p.A);
     a.W = static_cast<const uint16_t*>(p.W);
@@ -142,13 +243,35 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     a.act = p.act;
     a.out_f32 = p.out_f32 ? 1 : 0;
     a.eps = p.eps;
-    const int nwg = a.tiles_m * a.tiles_n;
+    a.splits = 1;
+    a.kchunk = a.K;
+    a.ws = nullptr;
+    a.cnt = nullptr;
+    if (c.splits > 1) {
+        // K steps per split, rounded up; the last split may get fewer
+        const int nk = a.K / pl.bk;
+        const int per = (nk + c.splits - 1) / c.splits;
+        a.splits = (nk + per - 1) / per;
+        a.kchunk = per * pl.bk;
+    }
+    if (a.splits > 1) {
+        const size_t tiles = (size_t)a.tiles_m * a.tiles_n;
+        const size_t nt = 256;
+        const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
+        const size_t acc_floats = nb * pl.bm * pl.bn;             // per tile and split
+        const size_t fm = pl.bm / 64;                             // row blocks per wave (RMS sums)
+        const size_t per_split = (acc_floats + nt * fm) * sizeof(float);
+        if (tiles >= kCounterBytes / sizeof(unsigned)) return hipErrorInvalidValue;
+        hipError_t e = get_workspace(stream, tiles * a.splits * per_split, &a.ws, &a.cnt);
+        if (e != hipSuccess) return e;
+    }
+    const int nwg = a.tiles_m * a.tiles_n * a.splits;
     const bool rms = p.op != Op::GemmEpilogue;
     const int K = a.K;
     const void* fn;
     if (p.op == Op::RmsSwiglu) fn = p.bf16 ? dual_fn<true>(pl, K) : dual_fn<false>(pl, K);
-    else if (p.bf16) fn = rms ? single_fn<true, true>(pl, K) : single_fn<true, false>(pl, K);
-    else fn = rms ? single_fn<false, true>(pl, K) : single_fn<false, false>(pl, K);
+    else if (p.bf16) fn = rms ? single_fn<true, true>(pl, K, a.splits > 1) : single_fn<true, false>(pl, K, a.splits > 1);
+    else fn = rms ? single_fn<false, true>(pl, K, a.splits > 1) : single_fn<false, false>(pl, K, a.splits > 1);
     return launch_fn(fn, a, nwg, 256, stream);
 }
 

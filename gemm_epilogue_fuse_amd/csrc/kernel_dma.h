@@ -39,6 +39,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor (gfx9 layout): base, stride 0, num_records bytes.
 __device__ __forceinline__ i32x4 rsrc128(const void* p, uint32_t bytes) {
@@ -55,7 +56,9 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16 bytes per lane, global -> LDS at m0 + 16*lane.
+// 16 bytes per lane, global -> LDS at m0 + 16*lane.  m0 is written here and
+// nowhere else in these kernels (the compiler does not use it on gfx950), so
+// clobbering it cannot disturb compiler-generated code.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
@@ -105,7 +108,7 @@ __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
     return o;
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, bool BF, bool RMS, int NB>
+template <int BM, int BN, int BK, int NS, int WM, int WN, bool BF, bool RMS, int NB, bool SPLIT>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_dma_kernel(const KArgs p) {
     constexpr int NT = WM * WN * 64;
@@ -136,9 +139,10 @@ gemm_dma_kernel(const KArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    int tm, tn, kz;
+    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, SPLIT ? p.splits : 1, tm, tn, kz);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = SPLIT ? kz * p.kchunk : 0;
     const int M = p.M, N = p.N, K = p.K;
 
     const i32x4 rsA = rsrc128(p.A + (size_t)m0 * K, (uint32_t)((size_t)(M - m0) * K * 2));
@@ -264,15 +268,15 @@ gemm_dma_kernel(const KArgs p) {
 
     constexpr int KS = BK / 16;
     constexpr int NMMA = NB * FM * FN;
-    const int nk = K / BK;
+    const int nk = (SPLIT ? min(p.kchunk, K - kbeg) : K) / BK;
     // Prologue: NS-1 stages in flight, wait for the first, queue the next.
     // Steps past the end of K are never computed; they re-read the last
     // tile so every address stays inside the tensors.
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s, min(s, nk - 1) * BK);
+    for (int s = 0; s < NS - 1; ++s) issue(s, kbeg + min(s, nk - 1) * BK);
     wait_vmcnt<(NS - 2) * LPT>();
     __syncthreads();
-    issue(NS - 1, min(NS - 1, nk - 1) * BK);
+    issue(NS - 1, kbeg + min(NS - 1, nk - 1) * BK);
     Frags F0, F1;
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, r);
@@ -298,7 +302,7 @@ gemm_dma_kernel(const KArgs p) {
         }
         const int rs_stage = more_in_stage ? kt % NS : (kt + 1) % NS;
         const int rs_ks = more_in_stage ? ks + 1 : 0;
-        const int k_dma = min(kt + NS, nk - 1) * BK;
+        const int k_dma = kbeg + min(kt + NS, nk - 1) * BK;
 #pragma unroll
         for (int m = 0; m < NMMA; ++m) {
             const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
@@ -327,6 +331,80 @@ gemm_dma_kernel(const KArgs p) {
     }
     wait_vmcnt<0>();
     __syncthreads();
+
+    if (SPLIT && p.splits > 1) {
+        // Split-K.  Every split stores its fp32 partial accumulators (and
+        // partial sums of squares) with device-coherent stores, waits for
+        // them to complete, then counts in on the tile's counter.  The last
+        // split to arrive adds the partials of splits 0..S-1 in that order --
+        // its own from registers at its place in the sequence -- so the sum
+        // does not depend on arrival order, and finishes the tile.  Device-
+        // scope relaxed atomics reach the coherence point directly, so no
+        // cache-wide write-back or invalidate is needed.
+        constexpr int NACC = NB * FM * FN * 16;  // floats per thread
+        const size_t split_floats = (size_t)NT * (NACC + FM);
+        const int tile = tm * p.tiles_n + tn;
+        float* part = p.ws + (size_t)tile * p.splits * split_floats;
+        float* mine = part + (size_t)kz * split_floats;
+        // Only outputs inside the [M, N] range travel (decode shapes fill a
+        // tile with a handful of rows).  Accumulator register r of a 32x32
+        // block holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
+        auto in_range = [&](int i, int j, int r) {
+            const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int col = n0 + wn * TN + j * 32 + (lane & 31);
+            return row < M && col < N;
+        };
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int e = ((o * FM + i) * FN + j) * 16 + r;
+                        if (in_range(i, j, r))
+                            __hip_atomic_store(mine + (size_t)e * NT + tid, acc[o][i][j][r], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    }
+        if constexpr (RMS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                __hip_atomic_store(mine + (size_t)(NACC + i) * NT + tid, ss[i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        __shared__ unsigned arrived;
+        if (tid == 0) arrived = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrived != (unsigned)(p.splits - 1)) return;
+        auto gather = [&](int e, float own) {
+            const float* src = part + (size_t)e * NT + tid;
+            float v = (kz == 0) ? own : __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int z = 1; z < p.splits; ++z)
+                v += (z == kz) ? own
+                               : __hip_atomic_load(src + (size_t)z * split_floats, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            return v;
+        };
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (in_range(i, j, r))
+                            acc[o][i][j][r] = gather(((o * FM + i) * FN + j) * 16 + r, acc[o][i][j][r]);
+        if constexpr (RMS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) ss[i] = gather(NACC + i, ss[i]);
+        }
+        // ready for the next call on this workspace (stream order separates calls)
+        if (tid == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     float* rs = reinterpret_cast<float*>(smem + NS * STAGE);
     if constexpr (RMS) {

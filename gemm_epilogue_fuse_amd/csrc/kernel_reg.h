@@ -55,8 +55,8 @@ gemm_fused_kernel(const KArgs p) {
     const int wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    int tm, tn;
-    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    int tm, tn, kz_unused;
+    map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, 1, tm, tn, kz_unused);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K;
 

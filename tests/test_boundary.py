@@ -131,7 +131,8 @@ def test_aliasing(L):
 
 def test_plans(L):
     assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
-    assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4"
+    assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4:k2"   # 128 tiles: split K in two
+    assert lf.plan_name(1, 1, 4096, 4096) == "dma_128x128x64_s4:k8"     # decode: 32 tiles
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
     assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"
@@ -147,6 +148,17 @@ def test_plans(L):
     finally:
         lf.set_plan(None)
     assert lf.plan_name(1, 64, 64, 64) == "dma_128x128x64_s4"
+    # forced split counts
+    lf.set_plan("dma_128x128x64_s4:k4")
+    try:
+        assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4:k4"
+        assert lf.plan_name(1, 512, 4096, 128) == "dma_128x128x64_s4:k2"  # at most one split per K step
+    finally:
+        lf.set_plan(None)
+    for bad in ("reg_128x128x64:k2", "dma_256x256x32_s4:k2", "dma_128x128x64_s4:x2", "dma_128x128x64_s4:k0", "dma_128x128x64_s4:k",
+                "dma_128x128x64_s4:k2x"):
+        with pytest.raises(lf.FuseError):
+            lf.set_plan(bad)
 
 
 def test_python_binding_rejects_bad_tensors():

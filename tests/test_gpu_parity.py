@@ -21,12 +21,25 @@ from parity_util import EPS, EPS32, assert_close, dev_t, sample_rows, say, to64
 
 pytestmark = pytest.mark.gpu
 
-PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64"]
+# Tile plans, and DMA plans with a forced split-K count (":k<S>"): the
+# splits of a tile are reduced in a fixed order by the last one to finish.
+PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64",
+         "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2"]
 
 
 def fitk(plan, K):
-    """DMA plans need K % 64 == 0: round K up for them (M and N stay ragged)."""
-    return -(-K // 64) * 64 if plan.startswith("dma") else K
+    """DMA plans need K % 64 == 0: round K up for them (M and N stay ragged);
+    split plans get at least 3 K steps per split."""
+    if not plan.startswith("dma"):
+        return K
+    K = -(-K // 64) * 64
+    if ":k" in plan:
+        K = max(K, 64 * 3 * int(plan.split(":k")[1]))
+    return K
+
+
+def base(plan):
+    return plan.split(":")[0]
 ACTS = ["none", "relu", "gelu_tanh", "silu"]
 
 
