@@ -330,7 +330,7 @@ def main():
         "hbm_frac": fields["hbm_frac"],
         "roofline": {"bound": "mfma", "achieved": fields["tflops"], "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": fields["mfma_frac"], "traffic": traffic,
-                     "algorithmic_bytes": alg, "kernel": "gemm_fused_kernel (plan %s)" % plan,
+                     "algorithmic_bytes": alg, "kernel": "%s (plan %s)" % ("gemm_dma_kernel" if plan.startswith("dma") else "gemm_fused_kernel", plan),
                      "kernel_source_sha256_16": kernel_hash()},
         "baseline_context": "0.208 ms fused on an NVIDIA A30 (page figure, other hardware); vs_baseline = 0.208 ms / ms_per_step",
     }

@@ -119,11 +119,14 @@ __device__ __forceinline__ void transpose_k8(const u32x4 (&in)[KB], u32x4 (&out)
 __device__ __forceinline__ float exp_fast(float x) {
     return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);
 }
-// GeLU, tanh form; tanh(u) = 1 - 2 / (exp(2u) + 1) saturates cleanly at +-1.
+// GeLU, tanh form.  0.5 z (1 + tanh u) = z * sigmoid(2u) = z / (1 + e^(-2u)) with
+// u = sqrt(2/pi) (z + 0.044715 z^3); -2u log2(e) = z (c0 + c1 z^2) feeds the exp2 unit
+// directly.  Saturates cleanly: e^(-2u) -> inf gives -0, -> 0 gives z.
 __device__ __forceinline__ float gelu_tanh(float z) {
-    const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);
-    const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(exp_fast(2.0f * u) + 1.0f);
-    return 0.5f * z * (1.0f + t);
+    constexpr float c0 = -2.302208198144325f;   // -2 sqrt(2/pi) log2(e)
+    constexpr float c1 = -0.1029432395800235f;  // c0 * 0.044715
+    const float e = __builtin_amdgcn_exp2f(z * __builtin_fmaf(c1, z * z, c0));
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + exp_fast(-z));
@@ -166,9 +169,10 @@ __device__ __forceinline__ void map_tile(int bid, int nwg, int tiles_m, int tile
 // holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32), are read back with
 // each lane owning 8 consecutive columns of one row, finished in fp32 (RMS
 // factor, bias, activation, residual; SiLU(gate)*up for the dual GEMM),
-// rounded once and written with 16-byte stores.  Each wave uses its own LDS
-// region of kStageFloats floats at `stage`; every thread of the workgroup
-// must call this.
+// rounded once and written with 16-byte stores.  The calling wave holds the
+// (wm, wn) wave tile of a WM x WN grid; each wave uses its own LDS region of
+// kStageFloats floats at `stage`; every thread of the workgroup must call
+// this.
 template <int BM, int BN, int WM, int WN, bool BF, bool RMS, int NB>
 struct TileStore {
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -181,10 +185,9 @@ struct TileStore {
 
     template <int ACT>
     static __device__ __forceinline__ void run_act(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
-                                                   const float* rs, int m0, int n0) {
+                                                   const float* rs, int m0, int n0, int wm, int wn) {
         const int lane = threadIdx.x & 63;
         const int wave = threadIdx.x >> 6;
-        const int wm = wave / WN, wn = wave % WN;
         const int M = p.M, N = p.N;
         float* stg = stage + wave * kStageFloats;
         const int ec = (lane % LPR) * 8;
@@ -258,15 +261,15 @@ struct TileStore {
     }
 
     static __device__ __forceinline__ void run(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
-                                               const float* rs, int m0, int n0) {
+                                               const float* rs, int m0, int n0, int wm, int wn) {
         if constexpr (NB == 2) {
-            run_act<0>(p, acc, stage, rs, m0, n0);
+            run_act<0>(p, acc, stage, rs, m0, n0, wm, wn);
         } else {
             switch (p.act) {
-            case 1: run_act<1>(p, acc, stage, rs, m0, n0); break;
-            case 2: run_act<2>(p, acc, stage, rs, m0, n0); break;
-            case 3: run_act<3>(p, acc, stage, rs, m0, n0); break;
-            default: run_act<0>(p, acc, stage, rs, m0, n0); break;
+            case 1: run_act<1>(p, acc, stage, rs, m0, n0, wm, wn); break;
+            case 2: run_act<2>(p, acc, stage, rs, m0, n0, wm, wn); break;
+            case 3: run_act<3>(p, acc, stage, rs, m0, n0, wm, wn); break;
+            default: run_act<0>(p, acc, stage, rs, m0, n0, wm, wn); break;
             }
         }
     }

@@ -41,28 +41,34 @@ using dev::KArgs;
 
 enum class Kind { Reg, Dma };
 
-// A tile plan: kernel family, tile sizes, K step, LDS stages, and whether
-// it can split K across workgroups.
+// A tile plan: kernel family, tile sizes, K step, LDS stages, wave grid
+// (wm x wn waves, kg K groups; the register-staged kernel always uses 2x2x1),
+// and whether it can split K across workgroups.
 struct Plan {
     const char* name;
     Kind kind;
     int bm, bn, bk, ns;
+    int wm, wn, kg;
     bool dual;
     bool split;
+    int threads() const { return wm * wn * kg * 64; }
 };
 
 constexpr Plan kPlans[] = {
-    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, false, false},
-    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, false, true},
-    {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, false, false},
-    {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, false, false},
-    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, true, false},
-    {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, true, false},
+    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, 2, 2, 1, false, false},
+    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, 2, 2, 1, false, true},
+    {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, 2, 2, 1, false, false},
+    {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, 2, 2, 1, false, false},
+    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 2, 2, 1, true, false},
+    {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, 2, 2, 1, true, false},
+    {"dma_256x256x32_s4_w8", Kind::Dma, 256, 256, 32, 4, 2, 4, 1, false, false},
+    {"dma_128x128x64_s4_g2", Kind::Dma, 128, 128, 64, 4, 2, 2, 2, false, true},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 
 std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
 std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
+
 
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
@@ -103,8 +109,17 @@ Choice choose(const Problem& p) {
         pl = (p.K % 32 == 0) ? &kPlans[4] : &kPlans[5];
     } else {
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        if (t256 >= 224) pl = (p.K % 32 == 0) ? &kPlans[0] : &kPlans[2];
-        else pl = (p.K % 64 == 0) ? &kPlans[1] : &kPlans[3];
+        if (t256 >= 224) {
+            pl = (p.K % 32 == 0) ? &kPlans[0] : &kPlans[2];
+        } else if (p.K % 64 == 0) {
+            // Outputs too small to fill the chip split K; their splits run
+            // the 8-wave tile, whose second K group keeps twice the LDS
+            // reads in flight.
+            const int s = auto_splits(kPlans[1], p);
+            return {s > 1 ? &kPlans[7] : &kPlans[1], s};
+        } else {
+            pl = &kPlans[3];
+        }
     }
     return {pl, auto_splits(*pl, p)};
 }
@@ -166,12 +181,18 @@ const void* reg_fn(int K) {
 
 template <bool BF, bool RMS>
 const void* single_fn(const Plan& pl, int K, bool split) {
+    using namespace dev;
     if (pl.kind == Kind::Dma) {
-        if (pl.bm == 256)
-            return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 256, 32, 4, 2, 2, BF, RMS, 1, false>);
-        if (split)
-            return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<128, 128, 64, 4, 2, 2, BF, RMS, 1, true>);
-        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<128, 128, 64, 4, 2, 2, BF, RMS, 1, false>);
+        if (pl.bm == 256) {
+            if (pl.wn == 4) return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, BF, RMS, 1, false>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 2, 1, BF, RMS, 1, false>);
+        }
+        if (pl.kg == 2) {
+            if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, BF, RMS, 1, true>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, BF, RMS, 1, false>);
+        }
+        if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, BF, RMS, 1, true>);
+        return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, BF, RMS, 1, false>);
     }
     if (pl.bm == 256) return reg_fn<256, 256, 2, 2, BF, RMS, 1, 1>(K);
     return reg_fn<128, 128, 2, 2, BF, RMS, 1, 2>(K);
@@ -180,7 +201,7 @@ const void* single_fn(const Plan& pl, int K, bool split) {
 template <bool BF>
 const void* dual_fn(const Plan& pl, int K) {
     if (pl.kind == Kind::Dma)
-        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, BF, true, 2, false>);
+        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, 1, BF, true, 2, false>);
     return reg_fn<256, 128, 2, 2, BF, true, 2, 1>(K);
 }
 
@@ -201,6 +222,7 @@ bool set_plan(const char* name) {
         g_override_splits.store(0);
         return true;
     }
+    // "<plan>" or "<plan>:k<S>", S in 1..64
     const char* colon = std::strchr(name, ':');
     const size_t len = colon ? (size_t)(colon - name) : std::strlen(name);
     int splits = 0;
@@ -256,11 +278,10 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     }
     if (a.splits > 1) {
         const size_t tiles = (size_t)a.tiles_m * a.tiles_n;
-        const size_t nt = 256;
         const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
-        const size_t acc_floats = nb * pl.bm * pl.bn;             // per tile and split
-        const size_t fm = pl.bm / 64;                             // row blocks per wave (RMS sums)
-        const size_t per_split = (acc_floats + nt * fm) * sizeof(float);
+        const size_t acc_floats = nb * pl.bm * pl.bn;                      // per tile and split
+        const size_t ss_floats = (size_t)pl.threads() * (pl.bm / pl.wm / 32 / pl.kg);  // RMS partial sums
+        const size_t per_split = (acc_floats + ss_floats) * sizeof(float);
         if (tiles >= kCounterBytes / sizeof(unsigned)) return hipErrorInvalidValue;
         hipError_t e = get_workspace(stream, tiles * a.splits * per_split, &a.ws, &a.cnt);
         if (e != hipSuccess) return e;
@@ -272,7 +293,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     if (p.op == Op::RmsSwiglu) fn = p.bf16 ? dual_fn<true>(pl, K) : dual_fn<false>(pl, K);
     else if (p.bf16) fn = rms ? single_fn<true, true>(pl, K, a.splits > 1) : single_fn<true, false>(pl, K, a.splits > 1);
     else fn = rms ? single_fn<false, true>(pl, K, a.splits > 1) : single_fn<false, false>(pl, K, a.splits > 1);
-    return launch_fn(fn, a, nwg, 256, stream);
+    return launch_fn(fn, a, nwg, pl.threads(), stream);
 }
 
 }  // namespace lf

@@ -23,9 +23,11 @@
 // Synchronisation per K step: wait until this wave's loads for the step have
 // landed (vmcnt), barrier (every wave's loads landed, every wave done with
 // the stage about to be refilled), issue the loads NS-1 steps ahead, compute.
-// The DMA and transposing reads are issued from inline assembly, so the
-// compiler neither waits for them (it does not know they are in flight) nor
-// reorders memory operations across them; the waits are explicit here.
+// The DMA is issued from inline assembly (it has no register result), so the
+// compiler neither waits for it nor reorders memory operations across it;
+// its waits are explicit here.  Fragment reads are ordinary LDS loads the
+// compiler tracks: an asm load would let the compiler copy its destination
+// register before the data has landed.
 //
 // Requires K % BK == 0 (the register-staged kernel covers other K).
 #pragma once
@@ -66,10 +68,15 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voff, u
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ u32x2 ds_tr16(uint32_t addr) {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-    return r;
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// ds_read_b64_tr_b16 through the compiler builtin, so the compiler knows the
+// load is in flight and waits for it before the result is used.
+__device__ __forceinline__ u32x2 ds_tr16(const char* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
 }
 
 template <int N>
@@ -108,13 +115,22 @@ __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
     return o;
 }
 
-template <int BM, int BN, int BK, int NS, int WM, int WN, bool BF, bool RMS, int NB, bool SPLIT>
-__global__ void __launch_bounds__(WM * WN * 64)
+// The workgroup is KG groups of WM x WN waves.  Group g computes the whole
+// BM x BN tile over its own share of every K step (16-wide sub-steps
+// g*KSG .. g*KSG+KSG-1 of each stage), so KG = 2 doubles the waves that keep
+// LDS reads in flight without shrinking the per-wave tile; the groups' sums
+// are added through LDS at the end, after which each wave owns FM/KG of its
+// row blocks.
+template <int BM, int BN, int BK, int NS, int WM, int WN, int KG, bool BF, bool RMS, int NB, bool SPLIT>
+__global__ void __launch_bounds__(WM * WN * KG * 64)
 gemm_dma_kernel(const KArgs p) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NWT = WM * WN;  // waves per K group
+    constexpr int NT = NWT * KG * 64;
     constexpr int NW = NT / 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int FMO = FM / KG;  // row blocks a wave owns after the group reduction
+    constexpr int KS = BK / 16, KSG = KS / KG;
     constexpr int ACH = BK / 8;
     constexpr int BCH = BN / 8;
     constexpr int A_BYTES = BM * BK * 2;
@@ -123,21 +139,32 @@ gemm_dma_kernel(const KArgs p) {
     constexpr int STAGE = G_OFF + (RMS ? 1024 : 0);
     constexpr int A_LD = A_BYTES / (NT * 16);
     constexpr int B_LD = B_BYTES / (NT * 16);
-    constexpr int LPT = A_LD + NB * B_LD + (RMS ? 1 : 0);
+    constexpr int LPT = A_LD + NB * B_LD + (RMS ? 1 : 0);  // DMA loads per thread and step
+    constexpr int NMMA = NB * FM * FN;
+    constexpr int NREAD = FM + 2 * NB * FN + (RMS ? 1 : 0);
+    constexpr int WIN = KSG * NMMA;  // matrix-core slots that carry one step's DMA
     static_assert(ACH == 4 || ACH == 8, "BK must be 32 or 64");
     static_assert(BCH >= 16, "BN must be at least 128 for the W swizzle");
     static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "tiles must split into 1 KiB DMA rows");
     static_assert(BK * 2 <= 1024, "gamma slot");
     static_assert((NS - 2) * LPT <= 63, "vmcnt range");
-    using Store = TileStore<BM, BN, WM, WN, BF, RMS, NB>;
+    static_assert(KG == 1 || KG == 2, "one or two K groups");
+    static_assert(FM % KG == 0 && KS % KG == 0, "groups split row blocks and sub-steps evenly");
+    static_assert(KSG % 2 == 0, "sub-steps per group and stage must be even so the fragment sets line up");
+    static_assert(WIN >= LPT, "one DMA row per matrix-core slot at most");
+    static_assert(KSG == 2 || KSG == 4, "two or four local sub-steps");
+    using Store = TileStore<BM, BN, WM * KG, WN, BF, RMS, NB>;
     static_assert(Store::kBytes <= NS * STAGE, "epilogue staging must fit in the LDS stages");
+    static_assert(KG == 1 || KG * NWT * FMO * (NB * FN * 16 + 1) * 64 * 4 <= NS * STAGE,
+                  "group reduction must fit in the LDS stages");
 
     __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + BM * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
+    const int g = KG == 1 ? 0 : wave / NWT, wl = KG == 1 ? wave : wave % NWT;
+    const int wm = wl / WN, wn = wl % WN;
 
     int tm, tn, kz;
     map_tile(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, SPLIT ? p.splits : 1, tm, tn, kz);
@@ -169,20 +196,23 @@ gemm_dma_kernel(const KArgs p) {
     }
     const uint32_t voffG = oob_or((uint32_t)lane * 16u, lane < ACH);
     const uint32_t lds0 = lds_u32(smem);
-
-    auto issue = [&](int s, int k0) {
+    // One DMA row of stage s (k offset k0): A rows, then W rows per operand,
+    // then gamma.
+    auto dma_piece = [&](int s, int k0, int d) {
         const uint32_t base = lds0 + (uint32_t)(s * STAGE);
-        const uint32_t sa = (uint32_t)k0 * 2u;
-        const uint32_t sw = (uint32_t)k0 * (uint32_t)N * 2u;
+        if (d < A_LD) {
+            dma16(rsA, base + (uint32_t)((d * NW + wave) * 1024), voffA[d], (uint32_t)k0 * 2u);
+        } else if (d < A_LD + NB * B_LD) {
+            const int o = (d - A_LD) / B_LD, i = (d - A_LD) % B_LD;
+            dma16(o ? rsW2 : rsW, base + (uint32_t)(A_BYTES + o * B_BYTES + (i * NW + wave) * 1024), voffB[i],
+                  (uint32_t)k0 * (uint32_t)N * 2u);
+        } else {
+            dma16(rsG, base + (uint32_t)G_OFF, voffG, (uint32_t)k0 * 2u);
+        }
+    };
+    auto issue = [&](int s, int k0) {
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) dma16(rsA, base + (uint32_t)((i * NW + wave) * 1024), voffA[i], sa);
-#pragma unroll
-        for (int o = 0; o < NB; ++o)
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i)
-                dma16(o ? rsW2 : rsW, base + (uint32_t)(A_BYTES + o * B_BYTES + (i * NW + wave) * 1024), voffB[i],
-                      sw);
-        if constexpr (RMS) dma16(rsG, base + (uint32_t)G_OFF, voffG, sa);
+        for (int d = 0; d < LPT; ++d) dma_piece(s, k0, d);
     };
 
     f32x16 acc[NB][FM][FN];
@@ -202,135 +232,185 @@ gemm_dma_kernel(const KArgs p) {
     int arow[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + (lane & 31);
-    const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);           // k-row within a 16-k step
+    const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);  // k-row within a 16-k step
     const int bcol = wn * TN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // Fragments of one 16-wide K sub-step, read from LDS by assembly so the
-    // waits below are the only ones: two sets alternate, the reads for
-    // sub-step t+1 (possibly in the next stage) are in flight while the
-    // matrix cores work on sub-step t.
+    // Fragments of one 16-wide K sub-step.  Two sets alternate: the reads
+    // for sub-step t+1 (possibly in the next stage) are in flight while the
+    // matrix cores work on sub-step t.  The reads are ordinary LDS loads, so
+    // the compiler tracks them and waits for each fragment right before its
+    // first use.
     struct Frags {
         u32x4 a[FM];
         u32x2 b0[NB][FN], b1[NB][FN];
         u32x4 g;
     };
-    // One LDS read of the fragments of sub-step ks of stage s: pieces
-    // 0..FM-1 are the A rows, then two transposing reads per (operand,
-    // column block), then gamma.
-    constexpr int NREAD = FM + 2 * NB * FN + (RMS ? 1 : 0);
+    // One LDS read of the fragments of sub-step ks of stage s.  Pieces come
+    // in the order the matrix cores consume them: A block 0 (and gamma),
+    // the transposing reads of every (operand, column block), then A blocks
+    // 1..FM-1.
+    constexpr int NRB = 2 * NB * FN;  // transposing reads per sub-step
     auto read_piece = [&](Frags& f, int s, int ks, int r) {
-        const uint32_t sbase = lds0 + (uint32_t)(s * STAGE);
+        const int sbase = s * STAGE;
         const int lc = 2 * ks + (lane >> 5);
-        if (r < FM) {
-            const int i = r;
-            const uint32_t addr = sbase + (uint32_t)(arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4));
-            asm volatile("ds_read_b128 %0, %1" : "=v"(f.a[i]) : "v"(addr) : "memory");
-        } else if (r < FM + 2 * NB * FN) {
-            const int t = r - FM;
+        constexpr int G0 = RMS ? 1 : 0;
+        if (r == 0 || r >= 1 + G0 + NRB) {
+            const int i = (r == 0) ? 0 : r - G0 - NRB;
+            const int off = sbase + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4);
+            f.a[i] = *reinterpret_cast<const u32x4*>(smem + off);
+        } else if (RMS && r == 1) {
+            f.g = *reinterpret_cast<const u32x4*>(smem + sbase + G_OFF + (lc << 4));
+        } else {
+            const int t = r - 1 - G0;
             const int o = t / (2 * FN), j = (t / 2) % FN, h = t & 1;
             const int kr = 16 * ks + bkr + 4 * h;
             const int n = bcol + 32 * j;
-            const uint32_t addr = sbase + (uint32_t)(A_BYTES + o * B_BYTES + kr * (BN * 2) +
-                                                     (((n >> 3) ^ swz_b(kr)) << 4) + (((n >> 2) & 1) << 3));
-            if (h == 0) f.b0[o][j] = ds_tr16(addr);
-            else f.b1[o][j] = ds_tr16(addr);
-        } else {
-            const uint32_t addr = sbase + (uint32_t)(G_OFF + (lc << 4));
-            asm volatile("ds_read_b128 %0, %1" : "=v"(f.g) : "v"(addr) : "memory");
+            const int off = sbase + A_BYTES + o * B_BYTES + kr * (BN * 2) + (((n >> 3) ^ swz_b(kr)) << 4) +
+                            (((n >> 2) & 1) << 3);
+            const u32x2 v = ds_tr16(smem + off);
+            if (h == 0) f.b0[o][j] = v;
+            else f.b1[o][j] = v;
         }
-    };
-    // One DMA row of stage s (k offset k0): A rows, then W rows per operand,
-    // then gamma.
-    auto dma_piece = [&](int s, int k0, int d) {
-        const uint32_t base = lds0 + (uint32_t)(s * STAGE);
-        if (d < A_LD) {
-            dma16(rsA, base + (uint32_t)((d * NW + wave) * 1024), voffA[d], (uint32_t)k0 * 2u);
-        } else if (d < A_LD + NB * B_LD) {
-            const int o = (d - A_LD) / B_LD, i = (d - A_LD) % B_LD;
-            dma16(o ? rsW2 : rsW, base + (uint32_t)(A_BYTES + o * B_BYTES + (i * NW + wave) * 1024), voffB[i],
-                  (uint32_t)k0 * (uint32_t)N * 2u);
-        } else {
-            dma16(rsG, base + (uint32_t)G_OFF, voffG, (uint32_t)k0 * 2u);
-        }
-    };
-    // Wait for every outstanding LDS read and tie the fragment registers to
-    // the wait, so nothing consumes them before it.
-    auto wait_frags = [&](Frags& f) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(f.a[i]));
-#pragma unroll
-        for (int o = 0; o < NB; ++o)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(f.b0[o][j]), "+v"(f.b1[o][j]));
-        if constexpr (RMS) asm volatile("" : "+v"(f.g));
     };
 
-    constexpr int KS = BK / 16;
-    constexpr int NMMA = NB * FM * FN;
     const int nk = (SPLIT ? min(p.kchunk, K - kbeg) : K) / BK;
     // Prologue: NS-1 stages in flight, wait for the first, queue the next.
     // Steps past the end of K are never computed; they re-read the last
     // tile so every address stays inside the tensors.
+    auto kstep = [&](int t) { return kbeg + min(t, nk - 1) * BK; };
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s, kbeg + min(s, nk - 1) * BK);
+    for (int s = 0; s < NS - 1; ++s) issue(s, kstep(s));
     wait_vmcnt<(NS - 2) * LPT>();
     __syncthreads();
-    issue(NS - 1, kbeg + min(NS - 1, nk - 1) * BK);
+    issue(NS - 1, kstep(NS - 1));
     Frags F0, F1;
 #pragma unroll
-    for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, r);
-    // Sub-step t = kt*KS + ks computes from fragment set t%2.  Its
-    // matrix-core instructions are interleaved one by one with the LDS reads
-    // of sub-step t+1 and, on the first sub-step of a stage, with the DMA of
-    // the stage NS-1 ahead, so neither the LDS queue nor the texture address
-    // FIFOs hold the matrix cores up.  When t+1 opens a new stage this wave
-    // first waits for its own loads of that stage, then a barrier makes every
-    // wave's loads visible and guarantees that no wave still reads the stage
-    // that the DMA is about to refill.
-    auto substep = [&](Frags& cur, Frags& nxt, int kt, int ks) {
-        wait_frags(cur);
-        if constexpr (RMS) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) cur.a[i] = rms_scale<BF>(cur.a[i], cur.g, ss[i]);
-        }
-        const bool more_in_stage = ks + 1 < KS;
-        const bool next_stage = !more_in_stage && kt + 1 < nk;
-        if (next_stage) {
+    for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, g * KSG, r);
+    // Local sub-step s of step kt computes group g's sub-step g*KSG+s from
+    // fragment set s%2.  Its matrix-core instructions are interleaved one by
+    // one with the LDS reads of the next local sub-step and with DMA rows, so
+    // neither the LDS queue nor the texture address path holds the matrix
+    // cores up.  On the last local sub-step of a step the wave first waits
+    // for its own loads of the next stage, then a barrier makes every wave's
+    // loads visible and guarantees that no wave still reads the current
+    // stage; the loads of step kt+NS into that stage are then spread over
+    // the WIN matrix-core slots from there to the end of step kt+1's
+    // second-to-last local sub-step (before the barrier that waits for them).
+    // FIRST / FINAL mark the first and last step, so the steady-state
+    // steps carry no conditions at all.
+    auto substep = [&](Frags& cur, Frags& nxt, int kt, auto S, auto FIRST, auto FINAL) {
+        constexpr int s = decltype(S)::value;
+        constexpr bool first = decltype(FIRST)::value, fin = decltype(FINAL)::value;
+        constexpr bool last = s == KSG - 1;
+        constexpr bool next_stage = last && !fin;
+        constexpr bool do_read = !last || next_stage;
+        constexpr bool do_dma = last ? !fin : !first;
+        constexpr int widx = last ? 0 : s + 1;
+        if constexpr (next_stage) {
             wait_vmcnt<(NS - 2) * LPT>();
             __syncthreads();
         }
-        const int rs_stage = more_in_stage ? kt % NS : (kt + 1) % NS;
-        const int rs_ks = more_in_stage ? ks + 1 : 0;
-        const int k_dma = kbeg + min(kt + NS, nk - 1) * BK;
+        const int rs_stage = last ? (kt + 1) % NS : kt % NS;
+        constexpr int rs_ks_local = last ? 0 : s + 1;
+        const int rs_ks = g * KSG + rs_ks_local;
+        const int dstep = last ? kt : kt - 1;
+        const int k_dma = kstep(dstep + NS);
 #pragma unroll
         for (int m = 0; m < NMMA; ++m) {
             const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
+            // A block i is scaled by gamma just before its first use
+            if constexpr (RMS)
+                if (o == 0 && j == 0) cur.a[i] = rms_scale<BF>(cur.a[i], cur.g, ss[i]);
             const u32x4 bfrag = {cur.b0[o][j][0], cur.b0[o][j][1], cur.b1[o][j][0], cur.b1[o][j][1]};
             acc[o][i][j] = mfma32<BF>(cur.a[i], bfrag, acc[o][i][j]);
             __builtin_amdgcn_sched_barrier(0);
-            if (m < NREAD && (more_in_stage || next_stage)) read_piece(nxt, rs_stage, rs_ks, m);
-            if (m < LPT && next_stage) dma_piece(kt % NS, k_dma, m);
+            if constexpr (do_read)
+                if (m < NREAD) read_piece(nxt, rs_stage, rs_ks, m);
+            if constexpr (do_dma) {
+#pragma unroll
+                for (int d = 0; d < LPT; ++d)
+                    if (widx * NMMA + m == (d * WIN) / LPT) dma_piece(dstep % NS, k_dma, d);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         // reads that did not fit between the matrix-core instructions
+        if constexpr (do_read) {
 #pragma unroll
-        for (int m = NMMA; m < NREAD; ++m)
-            if (more_in_stage || next_stage) read_piece(nxt, rs_stage, rs_ks, m);
-#pragma unroll
-        for (int m = NMMA; m < LPT; ++m)
-            if (next_stage) dma_piece(kt % NS, k_dma, m);
-    };
-    static_assert(KS % 2 == 0, "sub-steps per stage must be even so the fragment sets line up");
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ks += 2) {
-            substep(F0, F1, kt, ks);
-            substep(F1, F0, kt, ks + 1);
+            for (int m = NMMA; m < NREAD; ++m) read_piece(nxt, rs_stage, rs_ks, m);
         }
+    };
+    auto step = [&](int kt, auto FIRST, auto FINAL) {
+        substep(F0, F1, kt, ic<0>{}, FIRST, FINAL);
+        substep(F1, F0, kt, ic<1>{}, FIRST, FINAL);
+        if constexpr (KSG == 4) {
+            substep(F0, F1, kt, ic<2>{}, FIRST, FINAL);
+            substep(F1, F0, kt, ic<3>{}, FIRST, FINAL);
+        }
+    };
+    if (nk == 1) {
+        step(0, std::true_type{}, std::true_type{});
+    } else {
+        step(0, std::true_type{}, std::false_type{});
+        for (int kt = 1; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
+        step(nk - 1, std::false_type{}, std::true_type{});
     }
     wait_vmcnt<0>();
     __syncthreads();
+
+    // Add the K groups.  Wave (g, wm, wn) keeps row blocks g*FMO..g*FMO+FMO-1
+    // of its wave tile and hands the others to the wave of the other group
+    // through LDS (one region per writing group); the sum of a block is
+    // group 0's plus group 1's either way (fp32 addition commutes), so
+    // results do not depend on which wave adds.
+    f32x16 acco[NB][FMO][FN];
+    float sso[FMO];
+    if constexpr (KG == 1) {
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acco[o][i][j] = acc[o][i][j];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sso[i] = ss[i];
+    } else {
+        constexpr int RED = NWT * FMO * NB * FN * 16 * 64;  // floats per group
+        float* red = reinterpret_cast<float*>(smem);
+        float* sred = red + KG * RED;
+        float* red_mine = red + g * RED;
+        const float* red_other = red + (1 - g) * RED;
+        float* sred_mine = sred + g * NWT * FMO * 64;
+        const float* sred_other = sred + (1 - g) * NWT * FMO * 64;
+#pragma unroll
+        for (int i = 0; i < FMO; ++i) {
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        red_mine[((((wl * FMO + i) * NB + o) * FN + j) * 16 + r) * 64 + lane] =
+                            g ? acc[o][i][j][r] : acc[o][FMO + i][j][r];
+            if constexpr (RMS) sred_mine[(wl * FMO + i) * 64 + lane] = g ? ss[i] : ss[FMO + i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FMO; ++i) {
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acco[o][i][j][r] = (g ? acc[o][FMO + i][j][r] : acc[o][i][j][r]) +
+                                           red_other[((((wl * FMO + i) * NB + o) * FN + j) * 16 + r) * 64 + lane];
+            if constexpr (RMS) sso[i] = (g ? ss[FMO + i] : ss[i]) + sred_other[(wl * FMO + i) * 64 + lane];
+        }
+        __syncthreads();
+    }
+    // From here the wave holds the (wme, wn) tile of a (WM*KG) x WN grid.
+    constexpr int TME = TM / KG;
+    const int wme = wm * KG + g;
 
     if (SPLIT && p.splits > 1) {
         // Split-K.  Every split stores its fp32 partial accumulators (and
@@ -339,39 +419,46 @@ gemm_dma_kernel(const KArgs p) {
         // split to arrive adds the partials of splits 0..S-1 in that order --
         // its own from registers at its place in the sequence -- so the sum
         // does not depend on arrival order, and finishes the tile.  Device-
-        // scope relaxed atomics reach the coherence point directly, so no
+        // scope (sc1) accesses reach the coherence point directly, so no
         // cache-wide write-back or invalidate is needed.
-        constexpr int NACC = NB * FM * FN * 16;  // floats per thread
-        const size_t split_floats = (size_t)NT * (NACC + FM);
+        constexpr int NQ = NB * FMO * FN * 4;  // 16-byte groups per thread
+        constexpr int SPLIT_BYTES = NT * (NQ * 16 + FMO * 4);
         const int tile = tm * p.tiles_n + tn;
-        float* part = p.ws + (size_t)tile * p.splits * split_floats;
-        float* mine = part + (size_t)kz * split_floats;
-        // Only outputs inside the [M, N] range travel (decode shapes fill a
-        // tile with a handful of rows).  Accumulator register r of a 32x32
-        // block holds row 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
-        auto in_range = [&](int i, int j, int r) {
-            const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float* part = p.ws + (size_t)tile * p.splits * (SPLIT_BYTES / 4);
+        const __amdgpu_buffer_rsrc_t rsP = make_rsrc(part, (uint32_t)(p.splits * SPLIT_BYTES));
+        // Only groups of four rows that start inside [M, N] travel (decode
+        // shapes fill a tile with a handful of rows).  Accumulator register
+        // r of a 32x32 block holds row 8*(r/4) + 4*(lane/32) + r%4, column
+        // lane%32; registers 4q..4q+3 are one group.
+        auto in_range = [&](int i, int j, int q) {
+            const int row = m0 + wme * TME + i * 32 + 8 * q + 4 * (lane >> 5);
             const int col = n0 + wn * TN + j * 32 + (lane & 31);
             return row < M && col < N;
         };
+        const uint32_t own_off = (uint32_t)(kz * SPLIT_BYTES);
 #pragma unroll
         for (int o = 0; o < NB; ++o)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FMO; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int e = ((o * FM + i) * FN + j) * 16 + r;
-                        if (in_range(i, j, r))
-                            __hip_atomic_store(mine + (size_t)e * NT + tid, acc[o][i][j][r], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+                    for (int q = 0; q < 4; ++q) {
+                        const int e = ((o * FMO + i) * FN + j) * 4 + q;
+                        if (in_range(i, j, q)) {
+                            const u32x4 v = {__float_as_uint(acco[o][i][j][4 * q]),
+                                             __float_as_uint(acco[o][i][j][4 * q + 1]),
+                                             __float_as_uint(acco[o][i][j][4 * q + 2]),
+                                             __float_as_uint(acco[o][i][j][4 * q + 3])};
+                            __builtin_amdgcn_raw_buffer_store_b128(v, rsP, (uint32_t)((e * NT + tid) * 16), own_off,
+                                                                   16);
+                        }
                     }
         if constexpr (RMS) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                __hip_atomic_store(mine + (size_t)(NACC + i) * NT + tid, ss[i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < FMO; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sso[i]), rsP,
+                                                      (uint32_t)(NQ * NT * 16 + (i * NT + tid) * 4), own_off, 16);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -379,28 +466,45 @@ gemm_dma_kernel(const KArgs p) {
         if (tid == 0) arrived = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (arrived != (unsigned)(p.splits - 1)) return;
-        auto gather = [&](int e, float own) {
-            const float* src = part + (size_t)e * NT + tid;
-            float v = (kz == 0) ? own : __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int z = 1; z < p.splits; ++z)
-                v += (z == kz) ? own
-                               : __hip_atomic_load(src + (size_t)z * split_floats, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            return v;
-        };
 #pragma unroll
         for (int o = 0; o < NB; ++o)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FMO; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (in_range(i, j, r))
-                            acc[o][i][j][r] = gather(((o * FM + i) * FN + j) * 16 + r, acc[o][i][j][r]);
+                    for (int q = 0; q < 4; ++q) {
+                        if (!in_range(i, j, q)) continue;
+                        const int e = ((o * FMO + i) * FN + j) * 4 + q;
+                        const uint32_t voff = (uint32_t)((e * NT + tid) * 16);
+                        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+                        for (int z = 0; z < p.splits; ++z) {
+                            f32x4 v;
+                            if (z == kz) {
+                                v = f32x4{acco[o][i][j][4 * q], acco[o][i][j][4 * q + 1], acco[o][i][j][4 * q + 2],
+                                          acco[o][i][j][4 * q + 3]};
+                            } else {
+                                v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                  rsP, voff, (uint32_t)(z * SPLIT_BYTES), 16));
+                            }
+                            sum = (z == 0) ? v : sum + v;
+                        }
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) acco[o][i][j][4 * q + t] = sum[t];
+                    }
         if constexpr (RMS) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) ss[i] = gather(NACC + i, ss[i]);
+            for (int i = 0; i < FMO; ++i) {
+                float sum = 0.0f;
+                for (int z = 0; z < p.splits; ++z) {
+                    const float v = (z == kz) ? sso[i]
+                                              : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                    rsP, (uint32_t)(NQ * NT * 16 + (i * NT + tid) * 4),
+                                                    (uint32_t)(z * SPLIT_BYTES), 16));
+                    sum = (z == 0) ? v : sum + v;
+                }
+                sso[i] = sum;
+            }
         }
         // ready for the next call on this workspace (stream order separates calls)
         if (tid == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -408,15 +512,15 @@ gemm_dma_kernel(const KArgs p) {
 
     float* rs = reinterpret_cast<float*>(smem + NS * STAGE);
     if constexpr (RMS) {
-        // lanes l and l+32 hold the two k-halves of row l%32 of each fragment
+        // lanes l and l+32 hold the two k-halves of row l%32 of each block
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const float s = ss[i] + __shfl_xor(ss[i], 32);
-            if (wn == 0 && lane < 32) rs[arow[i]] = 1.0f / sqrtf(s / (float)K + p.eps);
+        for (int i = 0; i < FMO; ++i) {
+            const float s = sso[i] + __shfl_xor(sso[i], 32);
+            if (wn == 0 && lane < 32) rs[wme * TME + i * 32 + lane] = 1.0f / sqrtf(s / (float)K + p.eps);
         }
         __syncthreads();
     }
-    Store::run(p, acc, reinterpret_cast<float*>(smem), rs, m0, n0);
+    Store::run(p, acco, reinterpret_cast<float*>(smem), rs, m0, n0, wme, wn);
 }
 
 }  // namespace dev

@@ -268,7 +268,7 @@ gemm_fused_kernel(const KArgs p) {
 
     using Store = TileStore<BM, BN, WM, WN, BF, RMS, NB>;
     static_assert(Store::kBytes <= 2 * STAGE * 16, "staging must fit in the LDS stages");
-    Store::run(p, acc, reinterpret_cast<float*>(lds), rs, m0, n0);
+    Store::run(p, acc, reinterpret_cast<float*>(lds), rs, m0, n0, wm, wn);
 }
 
 }  // namespace dev

@@ -131,8 +131,8 @@ def test_aliasing(L):
 
 def test_plans(L):
     assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
-    assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4:k2"   # 128 tiles: split K in two
-    assert lf.plan_name(1, 1, 4096, 4096) == "dma_128x128x64_s4:k8"     # decode: 32 tiles
+    assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
+    assert lf.plan_name(1, 1, 4096, 4096) == "dma_128x128x64_s4_g2:k8"     # decode: 32 tiles
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
     assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 # Tile plans, and DMA plans with a forced split-K count (":k<S>"): the
 # splits of a tile are reduced in a fixed order by the last one to finish.
 PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64",
-         "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2"]
+         "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
+         "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3"]
 
 
 def fitk(plan, K):
