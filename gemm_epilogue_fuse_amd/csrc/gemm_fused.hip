@@ -184,15 +184,15 @@ const void* single_fn(const Plan& pl, int K, bool split) {
     using namespace dev;
     if (pl.kind == Kind::Dma) {
         if (pl.bm == 256) {
-            if (pl.wn == 4) return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, BF, RMS, 1, false>);
-            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 2, 1, BF, RMS, 1, false>);
+            if (pl.wn == 4) return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, false, BF, RMS, 1, false>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 2, 1, false, BF, RMS, 1, false>);
         }
         if (pl.kg == 2) {
-            if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, BF, RMS, 1, true>);
-            return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, BF, RMS, 1, false>);
+            if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, true, BF, RMS, 1, true>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, true, BF, RMS, 1, false>);
         }
-        if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, BF, RMS, 1, true>);
-        return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, BF, RMS, 1, false>);
+        if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, false, BF, RMS, 1, true>);
+        return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 1, false, BF, RMS, 1, false>);
     }
     if (pl.bm == 256) return reg_fn<256, 256, 2, 2, BF, RMS, 1, 1>(K);
     return reg_fn<128, 128, 2, 2, BF, RMS, 1, 2>(K);
@@ -201,7 +201,7 @@ const void* single_fn(const Plan& pl, int K, bool split) {
 template <bool BF>
 const void* dual_fn(const Plan& pl, int K) {
     if (pl.kind == Kind::Dma)
-        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, 1, BF, true, 2, false>);
+        return reinterpret_cast<const void*>(&dev::gemm_dma_kernel<256, 128, 32, 4, 2, 2, 1, false, BF, true, 2, false>);
     return reg_fn<256, 128, 2, 2, BF, true, 2, 1>(K);
 }
 

@@ -121,7 +121,7 @@ __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
 // LDS reads in flight without shrinking the per-wave tile; the groups' sums
 // are added through LDS at the end, after which each wave owns FM/KG of its
 // row blocks.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int KG, bool BF, bool RMS, int NB, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int KG, bool SRA, bool BF, bool RMS, int NB, bool SPLIT>
 __global__ void __launch_bounds__(WM * WN * KG * 64)
 gemm_dma_kernel(const KArgs p) {
     constexpr int NWT = WM * WN;  // waves per K group
@@ -150,9 +150,9 @@ gemm_dma_kernel(const KArgs p) {
     static_assert((NS - 2) * LPT <= 63, "vmcnt range");
     static_assert(KG == 1 || KG == 2, "one or two K groups");
     static_assert(FM % KG == 0 && KS % KG == 0, "groups split row blocks and sub-steps evenly");
-    static_assert(KSG % 2 == 0, "sub-steps per group and stage must be even so the fragment sets line up");
+    static_assert(NS >= 3, "two stages ahead of the one being read");
+    static_assert(SRA || KSG % 2 == 0, "sub-step read-ahead alternates fragment sets within a step");
     static_assert(WIN >= LPT, "one DMA row per matrix-core slot at most");
-    static_assert(KSG == 2 || KSG == 4, "two or four local sub-steps");
     using Store = TileStore<BM, BN, WM * KG, WN, BF, RMS, NB>;
     static_assert(Store::kBytes <= NS * STAGE, "epilogue staging must fit in the LDS stages");
     static_assert(KG == 1 || KG * NWT * FMO * (NB * FN * 16 + 1) * 64 * 4 <= NS * STAGE,
@@ -235,124 +235,190 @@ gemm_dma_kernel(const KArgs p) {
     const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);  // k-row within a 16-k step
     const int bcol = wn * TN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // Fragments of one 16-wide K sub-step.  Two sets alternate: the reads
-    // for sub-step t+1 (possibly in the next stage) are in flight while the
-    // matrix cores work on sub-step t.  The reads are ordinary LDS loads, so
-    // the compiler tracks them and waits for each fragment right before its
-    // first use.
+    // Fragment read-ahead.  SRA: two sets of a whole K step (the group's KSG
+    // sub-steps of 16) alternate, every read of step kt+1 in flight while the
+    // matrix cores work on step kt -- for few matrix-core instructions per
+    // sub-step.  Otherwise two sets of one sub-step alternate, the reads of
+    // sub-step t+1 in flight during sub-step t, which keeps the deepest DMA
+    // lookahead.  The reads are ordinary LDS loads, so the compiler tracks
+    // them and waits for each fragment right before its first use.
+    constexpr int KH = SRA ? KSG : 1;  // sub-steps one set holds
     struct Frags {
-        u32x4 a[FM];
-        u32x2 b0[NB][FN], b1[NB][FN];
-        u32x4 g;
+        u32x4 a[KH][FM];
+        u32x4 b[KH][NB][FN];  // k 0..3 of the lane's group from the first transposing read, 4..7 from the second
+        u32x4 g[KH];
     };
-    // One LDS read of the fragments of sub-step ks of stage s.  Pieces come
-    // in the order the matrix cores consume them: A block 0 (and gamma),
-    // the transposing reads of every (operand, column block), then A blocks
-    // 1..FM-1.
+    // One LDS read of local sub-step ls of stage s into slot h of a set.
+    // Pieces come in the order the matrix cores consume them: A block 0 (and
+    // gamma), the transposing reads of every (operand, column block), then A
+    // blocks 1..FM-1.
     constexpr int NRB = 2 * NB * FN;  // transposing reads per sub-step
-    auto read_piece = [&](Frags& f, int s, int ks, int r) {
+    auto read_piece = [&](Frags& f, int s, int ls, int h, int r) {
+        const int ks = g * KSG + ls;
         const int sbase = s * STAGE;
         const int lc = 2 * ks + (lane >> 5);
         constexpr int G0 = RMS ? 1 : 0;
         if (r == 0 || r >= 1 + G0 + NRB) {
             const int i = (r == 0) ? 0 : r - G0 - NRB;
             const int off = sbase + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4);
-            f.a[i] = *reinterpret_cast<const u32x4*>(smem + off);
+            f.a[h][i] = *reinterpret_cast<const u32x4*>(smem + off);
         } else if (RMS && r == 1) {
-            f.g = *reinterpret_cast<const u32x4*>(smem + sbase + G_OFF + (lc << 4));
+            f.g[h] = *reinterpret_cast<const u32x4*>(smem + sbase + G_OFF + (lc << 4));
         } else {
             const int t = r - 1 - G0;
-            const int o = t / (2 * FN), j = (t / 2) % FN, h = t & 1;
-            const int kr = 16 * ks + bkr + 4 * h;
+            const int o = t / (2 * FN), j = (t / 2) % FN, q = t & 1;
+            const int kr = 16 * ks + bkr + 4 * q;
             const int n = bcol + 32 * j;
             const int off = sbase + A_BYTES + o * B_BYTES + kr * (BN * 2) + (((n >> 3) ^ swz_b(kr)) << 4) +
                             (((n >> 2) & 1) << 3);
             const u32x2 v = ds_tr16(smem + off);
-            if (h == 0) f.b0[o][j] = v;
-            else f.b1[o][j] = v;
+            f.b[h][o][j][2 * q] = v[0];
+            f.b[h][o][j][2 * q + 1] = v[1];
         }
+    };
+    // The matrix-core instruction of slot m of a sub-step on slot h of a set.
+    auto mma = [&](Frags& cur, int h, int m) {
+        const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
+        // A block i is scaled by gamma just before its first use
+        if constexpr (RMS)
+            if (o == 0 && j == 0) cur.a[h][i] = rms_scale<BF>(cur.a[h][i], cur.g[h], ss[i]);
+        acc[o][i][j] = mfma32<BF>(cur.a[h][i], cur.b[h][o][j], acc[o][i][j]);
     };
 
     const int nk = (SPLIT ? min(p.kchunk, K - kbeg) : K) / BK;
-    // Prologue: NS-1 stages in flight, wait for the first, queue the next.
-    // Steps past the end of K are never computed; they re-read the last
-    // tile so every address stays inside the tensors.
     auto kstep = [&](int t) { return kbeg + min(t, nk - 1) * BK; };
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s, kstep(s));
-    wait_vmcnt<(NS - 2) * LPT>();
-    __syncthreads();
-    issue(NS - 1, kstep(NS - 1));
+    // Steps past the end of K are never computed; their loads re-read the
+    // last tile so every address stays inside the tensors.
     Frags F0, F1;
+    if constexpr (SRA) {
+        // Prologue: steps 0..NS-2 in flight, wait for the first, read it.
 #pragma unroll
-    for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, g * KSG, r);
-    // Local sub-step s of step kt computes group g's sub-step g*KSG+s from
-    // fragment set s%2.  Its matrix-core instructions are interleaved one by
-    // one with the LDS reads of the next local sub-step and with DMA rows, so
-    // neither the LDS queue nor the texture address path holds the matrix
-    // cores up.  On the last local sub-step of a step the wave first waits
-    // for its own loads of the next stage, then a barrier makes every wave's
-    // loads visible and guarantees that no wave still reads the current
-    // stage; the loads of step kt+NS into that stage are then spread over
-    // the WIN matrix-core slots from there to the end of step kt+1's
-    // second-to-last local sub-step (before the barrier that waits for them).
-    // FIRST / FINAL mark the first and last step, so the steady-state
-    // steps carry no conditions at all.
-    auto substep = [&](Frags& cur, Frags& nxt, int kt, auto S, auto FIRST, auto FINAL) {
-        constexpr int s = decltype(S)::value;
-        constexpr bool first = decltype(FIRST)::value, fin = decltype(FINAL)::value;
-        constexpr bool last = s == KSG - 1;
-        constexpr bool next_stage = last && !fin;
-        constexpr bool do_read = !last || next_stage;
-        constexpr bool do_dma = last ? !fin : !first;
-        constexpr int widx = last ? 0 : s + 1;
-        if constexpr (next_stage) {
-            wait_vmcnt<(NS - 2) * LPT>();
-            __syncthreads();
-        }
-        const int rs_stage = last ? (kt + 1) % NS : kt % NS;
-        constexpr int rs_ks_local = last ? 0 : s + 1;
-        const int rs_ks = g * KSG + rs_ks_local;
-        const int dstep = last ? kt : kt - 1;
-        const int k_dma = kstep(dstep + NS);
+        for (int s = 0; s < NS - 1; ++s) issue(s, kstep(s));
+        wait_vmcnt<(NS - 2) * LPT>();
+        __syncthreads();
 #pragma unroll
-        for (int m = 0; m < NMMA; ++m) {
-            const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
-            // A block i is scaled by gamma just before its first use
-            if constexpr (RMS)
-                if (o == 0 && j == 0) cur.a[i] = rms_scale<BF>(cur.a[i], cur.g, ss[i]);
-            const u32x4 bfrag = {cur.b0[o][j][0], cur.b0[o][j][1], cur.b1[o][j][0], cur.b1[o][j][1]};
-            acc[o][i][j] = mfma32<BF>(cur.a[i], bfrag, acc[o][i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (do_read)
-                if (m < NREAD) read_piece(nxt, rs_stage, rs_ks, m);
-            if constexpr (do_dma) {
+        for (int ls = 0; ls < KSG; ++ls)
 #pragma unroll
-                for (int d = 0; d < LPT; ++d)
-                    if (widx * NMMA + m == (d * WIN) / LPT) dma_piece(dstep % NS, k_dma, d);
+            for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, ls, ls, r);
+        // Step kt.  Unless it is the last: wait for this wave's loads of
+        // step kt+1, then a barrier makes every wave's loads visible and
+        // guarantees that no wave still reads stage kt-1 (its fragments were
+        // consumed in step kt-1).  The matrix-core instructions of step kt
+        // are interleaved one by one with the LDS reads of step kt+1 and with
+        // the DMA of step kt+NS-1 into the freed stage, each spread evenly
+        // over the WIN slots.  FINAL marks the last step, so the steady-state
+        // steps carry no conditions at all.
+        constexpr int RT = KSG * NREAD;  // fragment reads per step
+        auto step = [&](Frags& cur, Frags& nxt, int kt, auto FINAL) {
+            constexpr bool fin = decltype(FINAL)::value;
+            if constexpr (!fin) {
+                wait_vmcnt<(NS - 3) * LPT>();
+                __syncthreads();
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // reads that did not fit between the matrix-core instructions
-        if constexpr (do_read) {
+            const int rs_stage = (kt + 1) % NS;
+            const int dstage = (kt + NS - 1) % NS;
+            const int k_dma = kstep(kt + NS - 1);
 #pragma unroll
-            for (int m = NMMA; m < NREAD; ++m) read_piece(nxt, rs_stage, rs_ks, m);
+            for (int ls = 0; ls < KSG; ++ls) {
+#pragma unroll
+                for (int m = 0; m < NMMA; ++m) {
+                    mma(cur, ls, m);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (!fin) {
+                        const int slot = ls * NMMA + m;
+#pragma unroll
+                        for (int q = 0; q < RT; ++q)
+                            if ((q * WIN) / RT == slot) read_piece(nxt, rs_stage, q / NREAD, q / NREAD, q % NREAD);
+#pragma unroll
+                        for (int d = 0; d < LPT; ++d)
+                            if ((d * WIN) / LPT == slot) dma_piece(dstage, k_dma, d);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {
+            step(F0, F1, kt, std::false_type{});
+            step(F1, F0, kt + 1, std::false_type{});
         }
-    };
-    auto step = [&](int kt, auto FIRST, auto FINAL) {
-        substep(F0, F1, kt, ic<0>{}, FIRST, FINAL);
-        substep(F1, F0, kt, ic<1>{}, FIRST, FINAL);
-        if constexpr (KSG == 4) {
-            substep(F0, F1, kt, ic<2>{}, FIRST, FINAL);
-            substep(F1, F0, kt, ic<3>{}, FIRST, FINAL);
+        if (nk - kt == 2) {
+            step(F0, F1, kt, std::false_type{});
+            step(F1, F0, kt + 1, std::true_type{});
+        } else {
+            step(F0, F1, kt, std::true_type{});
         }
-    };
-    if (nk == 1) {
-        step(0, std::true_type{}, std::true_type{});
     } else {
-        step(0, std::true_type{}, std::false_type{});
-        for (int kt = 1; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
-        step(nk - 1, std::false_type{}, std::true_type{});
+        // Prologue: NS-1 stages in flight, wait for the first, queue the
+        // next, read the first sub-step.
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) issue(s, kstep(s));
+        wait_vmcnt<(NS - 2) * LPT>();
+        __syncthreads();
+        issue(NS - 1, kstep(NS - 1));
+#pragma unroll
+        for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, 0, r);
+        // Local sub-step s of step kt computes from set s%2.  Its
+        // matrix-core instructions are interleaved one by one with the LDS
+        // reads of the next local sub-step and with DMA rows.  On the last
+        // local sub-step of a step the wave first waits for its own loads of
+        // the next stage, then a barrier makes every wave's loads visible and
+        // guarantees that no wave still reads the current stage; the loads of
+        // step kt+NS into that stage are then spread over the WIN
+        // matrix-core slots from there to the end of step kt+1's
+        // second-to-last local sub-step (before the barrier that waits for
+        // them).  FIRST / FINAL mark the first and last step, so the
+        // steady-state steps carry no conditions at all.
+        auto substep = [&](Frags& cur, Frags& nxt, int kt, auto S, auto FIRST, auto FINAL) {
+            constexpr int s = decltype(S)::value;
+            constexpr bool first = decltype(FIRST)::value, fin = decltype(FINAL)::value;
+            constexpr bool last = s == KSG - 1;
+            constexpr bool next_stage = last && !fin;
+            constexpr bool do_read = !last || next_stage;
+            constexpr bool do_dma = last ? !fin : !first;
+            constexpr int widx = last ? 0 : s + 1;
+            if constexpr (next_stage) {
+                wait_vmcnt<(NS - 2) * LPT>();
+                __syncthreads();
+            }
+            const int rs_stage = last ? (kt + 1) % NS : kt % NS;
+            constexpr int rs_ls = last ? 0 : s + 1;
+            const int dstep = last ? kt : kt - 1;
+            const int k_dma = kstep(dstep + NS);
+#pragma unroll
+            for (int m = 0; m < NMMA; ++m) {
+                mma(cur, 0, m);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (do_read)
+                    if (m < NREAD) read_piece(nxt, rs_stage, rs_ls, 0, m);
+                if constexpr (do_dma) {
+#pragma unroll
+                    for (int d = 0; d < LPT; ++d)
+                        if (widx * NMMA + m == (d * WIN) / LPT) dma_piece(dstep % NS, k_dma, d);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // reads that did not fit between the matrix-core instructions
+            if constexpr (do_read) {
+#pragma unroll
+                for (int m = NMMA; m < NREAD; ++m) read_piece(nxt, rs_stage, rs_ls, 0, m);
+            }
+        };
+        auto step = [&](int kt, auto FIRST, auto FINAL) {
+            substep(F0, F1, kt, ic<0>{}, FIRST, FINAL);
+            substep(F1, F0, kt, ic<1>{}, FIRST, FINAL);
+            if constexpr (KSG == 4) {
+                substep(F0, F1, kt, ic<2>{}, FIRST, FINAL);
+                substep(F1, F0, kt, ic<3>{}, FIRST, FINAL);
+            }
+        };
+        if (nk == 1) {
+            step(0, std::true_type{}, std::true_type{});
+        } else {
+            step(0, std::true_type{}, std::false_type{});
+            for (int kt = 1; kt < nk - 1; ++kt) step(kt, std::false_type{}, std::false_type{});
+            step(nk - 1, std::false_type{}, std::true_type{});
+        }
     }
     wait_vmcnt<0>();
     __syncthreads();
