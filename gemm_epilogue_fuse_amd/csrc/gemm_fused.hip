@@ -32,6 +32,7 @@
 #include <utility>
 
 #include "kernel_dma.h"
+#include "kernel_decode.h"
 #include "kernel_reg.h"
 
 namespace lf {
@@ -39,7 +40,7 @@ namespace {
 
 using dev::KArgs;
 
-enum class Kind { Reg, Dma };
+enum class Kind { Reg, Dma, Dec };
 
 // A tile plan: kernel family, tile sizes, K step, LDS stages, wave grid
 // (wm x wn waves, kg K groups; the register-staged kernel always uses 2x2x1),
@@ -63,8 +64,16 @@ constexpr Plan kPlans[] = {
     {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, 2, 2, 1, true, false},
     {"dma_256x256x32_s4_w8", Kind::Dma, 256, 256, 32, 4, 2, 4, 1, false, false},
     {"dma_128x128x64_s4_g2", Kind::Dma, 128, 128, 64, 4, 2, 2, 2, false, true},
+    {"dma_128x128x32_s8_g2", Kind::Dma, 128, 128, 32, 8, 2, 2, 2, false, true},
+    {"dec_32x64", Kind::Dec, 32, 64, 64, 8, 1, 1, 4, false, true},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
+// Indices of the plans the automatic choice uses.
+enum PlanIndex : int {
+    kDma256 = 0, kDma128 = 1, kReg256 = 2, kReg128 = 3, kDual = 4, kRegDual = 5, kDma256W8 = 6, kDma128G2 = 7,
+    kDma128S8G2 = 8, kDec = 9
+};
+static_assert(kNumPlans == 10, "plan index table");
 
 std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
 std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
@@ -72,9 +81,16 @@ std::atomic<int> g_override_splits{0};  // forced split count with a forced plan
 
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
-    if (pl.kind == Kind::Dma && (p.K % pl.bk) != 0) return false;
+    if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
     return true;
 }
+
+// Rows up to which a call counts as decode-shaped: streaming W once at HBM
+// rate bounds it, and the small-M kernel serves it.
+constexpr int64_t kDecodeMaxM = 128;
+// K steps of 64 a small-M workgroup holds at most (its whole W chunk is in
+// flight at once).
+constexpr int kDecodeMaxSteps = 8;
 
 // Workgroups a plan keeps busy at once: the chip has 256 CUs and every
 // tile plan here holds one workgroup per CU.
@@ -87,9 +103,18 @@ struct Choice {
 
 // Split K when the output has too few tiles to occupy the CUs: the splits
 // of a tile run on different CUs and are reduced in a fixed order.  Each
-// split keeps at least 8 K steps so the pipeline has room to fill.
+// split keeps at least 8 K steps so the pipeline has room to fill.  The
+// small-M kernel takes the largest K chunk (at most 8 steps) that still
+// gives two workgroups per CU.
 int auto_splits(const Plan& pl, const Problem& p) {
     if (!pl.split) return 1;
+    if (pl.kind == Kind::Dec) {
+        const int64_t tiles = ((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn);
+        const int64_t nk = p.K / pl.bk;
+        int per = kDecodeMaxSteps;
+        while (per > 1 && tiles * ((nk + per - 1) / per) < 2 * kCUs) per /= 2;
+        return (int)((nk + per - 1) / per);
+    }
     const int64_t tiles = ((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn);
     const int64_t nk = p.K / pl.bk;
     int s = 1;
@@ -102,23 +127,30 @@ Choice choose(const Problem& p) {
     if (ov >= 0 && plan_fits(kPlans[ov], p)) {
         const int s = g_override_splits.load(std::memory_order_relaxed);
         const int64_t nk = p.K / kPlans[ov].bk;
+        if (kPlans[ov].kind == Kind::Dec) {
+            // the small-M kernel needs chunks of at most 8 steps
+            const int64_t lo = (nk + kDecodeMaxSteps - 1) / kDecodeMaxSteps;
+            return {&kPlans[ov], (int)std::min<int64_t>(std::max<int64_t>(s, lo), nk)};
+        }
         return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
     }
     const Plan* pl;
-    if (p.op == Op::RmsSwiglu) {
-        pl = (p.K % 32 == 0) ? &kPlans[4] : &kPlans[5];
+    if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0) {
+        pl = &kPlans[kDec];
+    } else if (p.op == Op::RmsSwiglu) {
+        pl = (p.K % 32 == 0) ? &kPlans[kDual] : &kPlans[kRegDual];
     } else {
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         if (t256 >= 224) {
-            pl = (p.K % 32 == 0) ? &kPlans[0] : &kPlans[2];
+            pl = (p.K % 32 == 0) ? &kPlans[kDma256] : &kPlans[kReg256];
         } else if (p.K % 64 == 0) {
             // Outputs too small to fill the chip split K; their splits run
             // the 8-wave tile, whose second K group keeps twice the LDS
             // reads in flight.
-            const int s = auto_splits(kPlans[1], p);
-            return {s > 1 ? &kPlans[7] : &kPlans[1], s};
+            const int s = auto_splits(kPlans[kDma128], p);
+            return {s > 1 ? &kPlans[kDma128G2] : &kPlans[kDma128], s};
         } else {
-            pl = &kPlans[3];
+            pl = &kPlans[kReg128];
         }
     }
     return {pl, auto_splits(*pl, p)};
@@ -186,6 +218,10 @@ const void* single_fn(const Plan& pl, int K, bool split) {
         if (pl.bm == 256) {
             if (pl.wn == 4) return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, false, BF, RMS, 1, false>);
             return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 2, 1, false, BF, RMS, 1, false>);
+        }
+        if (pl.kg == 2 && pl.bk == 32) {
+            if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 32, 8, 2, 2, 2, true, BF, RMS, 1, true>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 32, 8, 2, 2, 2, true, BF, RMS, 1, false>);
         }
         if (pl.kg == 2) {
             if (split) return reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 2, 2, 2, true, BF, RMS, 1, true>);
@@ -261,7 +297,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     a.K = (int)p.K;
     a.tiles_m = (int)((p.M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((p.N + pl.bn - 1) / pl.bn);
-    a.group_m = 4;
+    a.group_m = (pl.kind == Kind::Dec) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
     a.act = p.act;
     a.out_f32 = p.out_f32 ? 1 : 0;
     a.eps = p.eps;
@@ -281,7 +317,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
         const size_t acc_floats = nb * pl.bm * pl.bn;                      // per tile and split
         const size_t ss_floats = (size_t)pl.threads() * (pl.bm / pl.wm / 32 / pl.kg);  // RMS partial sums
-        const size_t per_split = (acc_floats + ss_floats) * sizeof(float);
+        const size_t per_split = (pl.kind == Kind::Dec) ? 256 * 36 : (acc_floats + ss_floats) * sizeof(float);
         if (tiles >= kCounterBytes / sizeof(unsigned)) return hipErrorInvalidValue;
         hipError_t e = get_workspace(stream, tiles * a.splits * per_split, &a.ws, &a.cnt);
         if (e != hipSuccess) return e;
@@ -290,6 +326,14 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     const bool rms = p.op != Op::GemmEpilogue;
     const int K = a.K;
     const void* fn;
+    if (pl.kind == Kind::Dec) {
+        using namespace dev;
+        fn = p.bf16 ? (rms ? reinterpret_cast<const void*>(&gemm_decode_kernel<64, true, true>)
+                           : reinterpret_cast<const void*>(&gemm_decode_kernel<64, true, false>))
+                    : (rms ? reinterpret_cast<const void*>(&gemm_decode_kernel<64, false, true>)
+                           : reinterpret_cast<const void*>(&gemm_decode_kernel<64, false, false>));
+        return launch_fn(fn, a, nwg, pl.threads(), stream);
+    }
     if (p.op == Op::RmsSwiglu) fn = p.bf16 ? dual_fn<true>(pl, K) : dual_fn<false>(pl, K);
     else if (p.bf16) fn = rms ? single_fn<true, true>(pl, K, a.splits > 1) : single_fn<true, false>(pl, K, a.splits > 1);
     else fn = rms ? single_fn<false, true>(pl, K, a.splits > 1) : single_fn<false, false>(pl, K, a.splits > 1);

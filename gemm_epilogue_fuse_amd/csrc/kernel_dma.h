@@ -249,15 +249,21 @@ gemm_dma_kernel(const KArgs p) {
         u32x4 g[KH];
     };
     // One LDS read of local sub-step ls of stage s into slot h of a set.
-    // Pieces come in the order the matrix cores consume them: A block 0 (and
-    // gamma), the transposing reads of every (operand, column block), then A
-    // blocks 1..FM-1.
+    // With sub-step read-ahead pieces come in the order the matrix cores
+    // consume them: A block 0 (and gamma), the transposing reads of every
+    // (operand, column block), then A blocks 1..FM-1.  With step read-ahead
+    // A blocks and gamma come first, so they can be scaled early.
     constexpr int NRB = 2 * NB * FN;  // transposing reads per sub-step
+    constexpr int G0 = RMS ? 1 : 0;
     auto read_piece = [&](Frags& f, int s, int ls, int h, int r) {
         const int ks = g * KSG + ls;
         const int sbase = s * STAGE;
         const int lc = 2 * ks + (lane >> 5);
-        constexpr int G0 = RMS ? 1 : 0;
+        if (SRA) {
+            // order: A0, gamma, A1..A(FM-1), B pieces -> map to the other order's numbering
+            if (r >= 1 + G0 && r < G0 + FM) r = r - G0 - 1 + 1 + G0 + NRB;          // A1..
+            else if (r >= G0 + FM) r = r - (G0 + FM) + 1 + G0;                      // B pieces
+        }
         if (r == 0 || r >= 1 + G0 + NRB) {
             const int i = (r == 0) ? 0 : r - G0 - NRB;
             const int off = sbase + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4);
@@ -276,11 +282,13 @@ gemm_dma_kernel(const KArgs p) {
             f.b[h][o][j][2 * q + 1] = v[1];
         }
     };
-    // The matrix-core instruction of slot m of a sub-step on slot h of a set.
+    // The matrix-core instruction of slot m of a sub-step on slot h of a
+    // set.  With sub-step read-ahead A block i is scaled by gamma just before
+    // its first use; with step read-ahead the scaling runs a sub-step ahead
+    // (see below).
     auto mma = [&](Frags& cur, int h, int m) {
         const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
-        // A block i is scaled by gamma just before its first use
-        if constexpr (RMS)
+        if constexpr (RMS && !SRA)
             if (o == 0 && j == 0) cur.a[h][i] = rms_scale<BF>(cur.a[h][i], cur.g[h], ss[i]);
         acc[o][i][j] = mfma32<BF>(cur.a[h][i], cur.b[h][o][j], acc[o][i][j]);
     };
@@ -300,14 +308,21 @@ gemm_dma_kernel(const KArgs p) {
         for (int ls = 0; ls < KSG; ++ls)
 #pragma unroll
             for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, ls, ls, r);
+        if constexpr (RMS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) F0.a[0][i] = rms_scale<BF>(F0.a[0][i], F0.g[0], ss[i]);
+        }
         // Step kt.  Unless it is the last: wait for this wave's loads of
         // step kt+1, then a barrier makes every wave's loads visible and
         // guarantees that no wave still reads stage kt-1 (its fragments were
         // consumed in step kt-1).  The matrix-core instructions of step kt
         // are interleaved one by one with the LDS reads of step kt+1 and with
         // the DMA of step kt+NS-1 into the freed stage, each spread evenly
-        // over the WIN slots.  FINAL marks the last step, so the steady-state
-        // steps carry no conditions at all.
+        // over the WIN slots.  RMS: the A blocks of the following sub-step
+        // (the next step's first, on the last sub-step) are scaled by gamma
+        // in the slots of the current one, off the matrix cores' dependency
+        // path.  FINAL marks the last step, so the steady-state steps carry
+        // no conditions at all.
         constexpr int RT = KSG * NREAD;  // fragment reads per step
         auto step = [&](Frags& cur, Frags& nxt, int kt, auto FINAL) {
             constexpr bool fin = decltype(FINAL)::value;
@@ -332,6 +347,14 @@ gemm_dma_kernel(const KArgs p) {
 #pragma unroll
                         for (int d = 0; d < LPT; ++d)
                             if ((d * WIN) / LPT == slot) dma_piece(dstage, k_dma, d);
+                    }
+                    if constexpr (RMS) {
+                        // block i of the following sub-step at slot NMMA-FM+i
+                        const int i = m - (NMMA - FM);
+                        if (i >= 0) {
+                            if (ls + 1 < KSG) cur.a[ls + 1][i] = rms_scale<BF>(cur.a[ls + 1][i], cur.g[ls + 1], ss[i]);
+                            else if (!fin) nxt.a[0][i] = rms_scale<BF>(nxt.a[0][i], nxt.g[0], ss[i]);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }

@@ -132,7 +132,7 @@ def test_aliasing(L):
 def test_plans(L):
     assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
-    assert lf.plan_name(1, 1, 4096, 4096) == "dma_128x128x64_s4_g2:k8"     # decode: 32 tiles
+    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"     # decode: small-M kernel, 64 tiles x 8 K chunks
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
     assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"
@@ -147,7 +147,10 @@ def test_plans(L):
         assert lf.plan_name(2, 64, 128, 64) == "dma_dual_256x128x32_s4"
     finally:
         lf.set_plan(None)
-    assert lf.plan_name(1, 64, 64, 64) == "dma_128x128x64_s4"
+    assert lf.plan_name(1, 64, 64, 64) == "dec_32x64"
+    assert lf.plan_name(1, 128, 1024, 1024) == "dec_32x64:k8"   # 4 x 16 tiles, K chunks of 2 steps: 512 workgroups
+    assert lf.plan_name(1, 129, 4096, 4096) == "dma_128x128x64_s4_g2:k4"  # beyond decode rows
+    assert lf.plan_name(2, 1, 256, 4096) == "dma_dual_256x128x32_s4"     # the dual GEMM has no small-M kernel
     # forced split counts
     lf.set_plan("dma_128x128x64_s4:k4")
     try:
