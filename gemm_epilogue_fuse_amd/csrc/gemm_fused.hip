@@ -33,6 +33,7 @@
 
 #include "kernel_dma.h"
 #include "kernel_decode.h"
+#include "kernel_strip.h"
 #include "kernel_reg.h"
 
 namespace lf {
@@ -40,7 +41,7 @@ namespace {
 
 using dev::KArgs;
 
-enum class Kind { Reg, Dma, Dec };
+enum class Kind { Reg, Dma, Dec, Strip };
 
 // A tile plan: kernel family, tile sizes, K step, LDS stages, wave grid
 // (wm x wn waves, kg K groups; the register-staged kernel always uses 2x2x1),
@@ -66,14 +67,16 @@ constexpr Plan kPlans[] = {
     {"dma_128x128x64_s4_g2", Kind::Dma, 128, 128, 64, 4, 2, 2, 2, false, true},
     {"dma_128x128x32_s8_g2", Kind::Dma, 128, 128, 32, 8, 2, 2, 2, false, true},
     {"dec_32x64", Kind::Dec, 32, 64, 64, 8, 1, 1, 4, false, true},
+    {"strip_16x16", Kind::Strip, 16, 16, 128, 16, 1, 1, 4, false, false},
+    {"strip_32x16", Kind::Strip, 32, 16, 128, 11, 1, 1, 4, false, false},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 // Indices of the plans the automatic choice uses.
 enum PlanIndex : int {
     kDma256 = 0, kDma128 = 1, kReg256 = 2, kReg128 = 3, kDual = 4, kRegDual = 5, kDma256W8 = 6, kDma128G2 = 7,
-    kDma128S8G2 = 8, kDec = 9
+    kDma128S8G2 = 8, kDec = 9, kStrip16 = 10, kStrip32 = 11
 };
-static_assert(kNumPlans == 10, "plan index table");
+static_assert(kNumPlans == 12, "plan index table");
 
 std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
 std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
@@ -82,6 +85,7 @@ std::atomic<int> g_override_splits{0};  // forced split count with a forced plan
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
     if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
+    if (pl.kind == Kind::Strip && p.op != Op::GemmEpilogue && p.K > dev::kStripMaxK) return false;
     return true;
 }
 
@@ -135,7 +139,12 @@ Choice choose(const Problem& p) {
         return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
     }
     const Plan* pl;
-    if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0) {
+    if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kStrip16], p)) {
+        // a few rows and a short K: one workgroup per 16-column strip over
+        // all of K (no partial sums cross the device); longer K walks too
+        // many steps per workgroup and splits K instead
+        pl = p.M <= 16 ? &kPlans[kStrip16] : &kPlans[kStrip32];
+    } else if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0) {
         pl = &kPlans[kDec];
     } else if (p.op == Op::RmsSwiglu) {
         pl = (p.K % 32 == 0) ? &kPlans[kDual] : &kPlans[kRegDual];
@@ -297,7 +306,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     a.K = (int)p.K;
     a.tiles_m = (int)((p.M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((p.N + pl.bn - 1) / pl.bn);
-    a.group_m = (pl.kind == Kind::Dec) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
+    a.group_m = (pl.kind == Kind::Dec || pl.kind == Kind::Strip) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
     a.act = p.act;
     a.out_f32 = p.out_f32 ? 1 : 0;
     a.eps = p.eps;
@@ -326,6 +335,20 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     const bool rms = p.op != Op::GemmEpilogue;
     const int K = a.K;
     const void* fn;
+    if (pl.kind == Kind::Strip) {
+        using namespace dev;
+        if (pl.bm == 16)
+            fn = p.bf16 ? (rms ? reinterpret_cast<const void*>(&gemm_strip_kernel<1, 16, true, true>)
+                               : reinterpret_cast<const void*>(&gemm_strip_kernel<1, 16, true, false>))
+                        : (rms ? reinterpret_cast<const void*>(&gemm_strip_kernel<1, 16, false, true>)
+                               : reinterpret_cast<const void*>(&gemm_strip_kernel<1, 16, false, false>));
+        else
+            fn = p.bf16 ? (rms ? reinterpret_cast<const void*>(&gemm_strip_kernel<2, 11, true, true>)
+                               : reinterpret_cast<const void*>(&gemm_strip_kernel<2, 11, true, false>))
+                        : (rms ? reinterpret_cast<const void*>(&gemm_strip_kernel<2, 11, false, true>)
+                               : reinterpret_cast<const void*>(&gemm_strip_kernel<2, 11, false, false>));
+        return launch_fn(fn, a, nwg, pl.threads(), stream);
+    }
     if (pl.kind == Kind::Dec) {
         using namespace dev;
         fn = p.bf16 ? (rms ? reinterpret_cast<const void*>(&gemm_decode_kernel<64, true, true>)

@@ -132,7 +132,10 @@ def test_aliasing(L):
 def test_plans(L):
     assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
-    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"     # decode: small-M kernel, 64 tiles x 8 K chunks
+    assert lf.plan_name(1, 1, 1024, 1024) == "strip_16x16"      # decode, a few rows, short K: column strips over all of K
+    assert lf.plan_name(1, 32, 1024, 1024, lf.BF16) == "strip_32x16"
+    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, 8 K chunks
+    assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k16"
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
     assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"

@@ -22,15 +22,16 @@ pytestmark = pytest.mark.gpu
 PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64",
          "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
          "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
-         "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3"]
+         "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
+         "strip_16x16", "strip_32x16"]
 
 
 def fitk(plan, K):
-    """DMA and small-M plans need K % 64 == 0: round K up for them (M and N stay ragged);
+    """DMA and small-M plans need K % 64 == 0 (strips K % 128): round K up for them (M and N stay ragged);
     split plans get at least 3 K steps per split."""
-    if not plan.startswith(("dma", "dec")):
+    if not plan.startswith(("dma", "dec", "strip")):
         return K
-    K = -(-K // 64) * 64
+    K = -(-K // (128 if plan.startswith("strip") else 64)) * (128 if plan.startswith("strip") else 64)
     if plan.startswith("dec") and ":k" not in plan:
         K = min(K, 512)  # one K chunk: at most 8 steps of 64
     if ":k" in plan:
