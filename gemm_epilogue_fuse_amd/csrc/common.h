@@ -62,9 +62,16 @@ __device__ __forceinline__ uint16_t f32_h(float x) {
     if constexpr (BF) return __builtin_bit_cast(uint16_t, (__bf16)x);
     else return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
+// Two values rounded to the 16-bit type (nearest even) and packed, low half
+// first: one v_cvt_pk_{f16,bf16}_f32.
 template <bool BF>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f32_h<BF>(a) | ((uint32_t)f32_h<BF>(b) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    if constexpr (BF) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
 template <bool BF>

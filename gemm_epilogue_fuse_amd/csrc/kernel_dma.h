@@ -92,8 +92,12 @@ __device__ __forceinline__ int swz_a(int r) {
 __device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
 
 // x * gamma, rounded to the 16-bit type (nearest even), and sum x^2 in fp32.
-// (Vector elements are copied to scalars before __builtin_bit_cast: applied
-// to an element subscript directly, clang takes element 0 every time.)
+// bf16 has no packed multiply, so each product comes from a two-term dot
+// product against gamma with the other half zeroed: a bf16 x bf16 product is
+// exact in fp32, so this equals the fp32 multiply, and the one rounding is the
+// conversion back to bf16.  (Vector elements are copied to scalars before
+// __builtin_bit_cast: applied to an element subscript directly, clang takes
+// element 0 every time.)
 template <bool BF>
 __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
     u32x4 o;
@@ -104,7 +108,12 @@ __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
         if constexpr (BF) {
             const bf16x2 xv = __builtin_bit_cast(bf16x2, xq);
             ss = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, ss, false);
-            o[q] = pack2<true>(lo_f32<true>(xq) * lo_f32<true>(gq), hi_f32<true>(xq) * hi_f32<true>(gq));
+            // (compiler builtins, not inline assembly: x comes from an LDS
+            // read the compiler must see consumed to place its wait)
+            const float plo = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, gq & 0xffffu), 0.0f, false);
+            const float phi =
+                __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, gq & 0xffff0000u), 0.0f, false);
+            o[q] = pack2<true>(plo, phi);
         } else {
             const f16x2 xv = __builtin_bit_cast(f16x2, xq);
             ss = __builtin_amdgcn_fdot2(xv, xv, ss, false);
