@@ -95,6 +95,10 @@ constexpr int64_t kDecodeMaxM = 128;
 // K steps of 64 a small-M workgroup holds at most (its whole W chunk is in
 // flight at once).
 constexpr int kDecodeMaxSteps = 8;
+// The small-M kernel reads W once per 32-row tile.  Past this much W traffic
+// the 128-row split tile, which reads W once per 128 rows, is faster (the
+// crossover lies between 33 rows at 4096x4096 and 128 rows at 2048x2048).
+constexpr int64_t kDecodeMaxWBytes = int64_t(32) << 20;
 
 // Workgroups a plan keeps busy at once: the chip has 256 CUs and every
 // tile plan here holds one workgroup per CU.
@@ -113,11 +117,10 @@ struct Choice {
 int auto_splits(const Plan& pl, const Problem& p) {
     if (!pl.split) return 1;
     if (pl.kind == Kind::Dec) {
-        const int64_t tiles = ((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn);
-        const int64_t nk = p.K / pl.bk;
-        int per = kDecodeMaxSteps;
-        while (per > 1 && tiles * ((nk + per - 1) / per) < 2 * kCUs) per /= 2;
-        return (int)((nk + per - 1) / per);
+        // Longest chunks the kernel holds: measured on 1..128 rows and
+        // K = 1024..4096, every further split (more workgroups, shorter
+        // chunks) costs more in partial-sum traffic than it gains.
+        return (int)((p.K / pl.bk + kDecodeMaxSteps - 1) / kDecodeMaxSteps);
     }
     const int64_t tiles = ((p.M + pl.bm - 1) / pl.bm) * ((p.N + pl.bn - 1) / pl.bn);
     const int64_t nk = p.K / pl.bk;
@@ -143,8 +146,9 @@ Choice choose(const Problem& p) {
         // a few rows and a short K: one workgroup per 16-column strip over
         // all of K (no partial sums cross the device); longer K walks too
         // many steps per workgroup and splits K instead
-        pl = p.M <= 16 ? &kPlans[kStrip16] : &kPlans[kStrip32];
-    } else if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0) {
+        pl = &kPlans[kStrip16];
+    } else if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0 &&
+               ((p.M + 31) / 32) * p.K * p.N * 2 <= kDecodeMaxWBytes) {
         pl = &kPlans[kDec];
     } else if (p.op == Op::RmsSwiglu) {
         pl = (p.K % 32 == 0) ? &kPlans[kDual] : &kPlans[kRegDual];

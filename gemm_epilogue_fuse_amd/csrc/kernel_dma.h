@@ -564,45 +564,66 @@ gemm_dma_kernel(const KArgs p) {
         if (tid == 0) arrived = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (arrived != (unsigned)(p.splits - 1)) return;
+        // Sum the partials in split order 0..S-1.  Each pass issues all of one
+        // split's loads before using any, so a split costs one round trip to
+        // the coherence point rather than one per 16-byte group.
+        f32x16 sum[NB][FMO][FN];
+        float ssum[FMO];
+        for (int z = 0; z < p.splits; ++z) {
+            const uint32_t zoff = (uint32_t)(z * SPLIT_BYTES);
+            f32x16 v[NB][FMO][FN];
+            float vs[FMO];
+            if (z == kz) {
+#pragma unroll
+                for (int o = 0; o < NB; ++o)
+#pragma unroll
+                    for (int i = 0; i < FMO; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) v[o][i][j] = acco[o][i][j];
+#pragma unroll
+                for (int i = 0; i < FMO; ++i) vs[i] = sso[i];
+            } else {
+#pragma unroll
+                for (int o = 0; o < NB; ++o)
+#pragma unroll
+                    for (int i = 0; i < FMO; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+                                if (in_range(i, j, q)) {
+                                    const int e = ((o * FMO + i) * FN + j) * 4 + q;
+                                    t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      rsP, (uint32_t)((e * NT + tid) * 16), zoff, 16));
+                                }
+#pragma unroll
+                                for (int t4 = 0; t4 < 4; ++t4) v[o][i][j][4 * q + t4] = t[t4];
+                            }
+#pragma unroll
+                for (int i = 0; i < FMO; ++i)
+                    vs[i] = RMS ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                      rsP, (uint32_t)(NQ * NT * 16 + (i * NT + tid) * 4), zoff, 16))
+                                : 0.0f;
+            }
+#pragma unroll
+            for (int o = 0; o < NB; ++o)
+#pragma unroll
+                for (int i = 0; i < FMO; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) sum[o][i][j] = (z == 0) ? v[o][i][j] : sum[o][i][j] + v[o][i][j];
+#pragma unroll
+            for (int i = 0; i < FMO; ++i) ssum[i] = (z == 0) ? vs[i] : ssum[i] + vs[i];
+        }
 #pragma unroll
         for (int o = 0; o < NB; ++o)
 #pragma unroll
             for (int i = 0; i < FMO; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        if (!in_range(i, j, q)) continue;
-                        const int e = ((o * FMO + i) * FN + j) * 4 + q;
-                        const uint32_t voff = (uint32_t)((e * NT + tid) * 16);
-                        f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-                        for (int z = 0; z < p.splits; ++z) {
-                            f32x4 v;
-                            if (z == kz) {
-                                v = f32x4{acco[o][i][j][4 * q], acco[o][i][j][4 * q + 1], acco[o][i][j][4 * q + 2],
-                                          acco[o][i][j][4 * q + 3]};
-                            } else {
-                                v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                  rsP, voff, (uint32_t)(z * SPLIT_BYTES), 16));
-                            }
-                            sum = (z == 0) ? v : sum + v;
-                        }
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) acco[o][i][j][4 * q + t] = sum[t];
-                    }
+                for (int j = 0; j < FN; ++j) acco[o][i][j] = sum[o][i][j];
         if constexpr (RMS) {
 #pragma unroll
-            for (int i = 0; i < FMO; ++i) {
-                float sum = 0.0f;
-                for (int z = 0; z < p.splits; ++z) {
-                    const float v = (z == kz) ? sso[i]
-                                              : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                                    rsP, (uint32_t)(NQ * NT * 16 + (i * NT + tid) * 4),
-                                                    (uint32_t)(z * SPLIT_BYTES), 16));
-                    sum = (z == 0) ? v : sum + v;
-                }
-                sso[i] = sum;
-            }
+            for (int i = 0; i < FMO; ++i) sso[i] = ssum[i];
         }
         // ready for the next call on this workspace (stream order separates calls)
         if (tid == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

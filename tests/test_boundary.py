@@ -133,9 +133,13 @@ def test_plans(L):
     assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
     assert lf.plan_name(1, 1, 1024, 1024) == "strip_16x16"      # decode, a few rows, short K: column strips over all of K
-    assert lf.plan_name(1, 32, 1024, 1024, lf.BF16) == "strip_32x16"
-    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, 8 K chunks
-    assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k16"
+    assert lf.plan_name(1, 32, 1024, 1024, lf.BF16) == "strip_16x16"  # two row tiles of 16 still beat one of 32
+    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, K chunks of 8 steps
+    assert lf.plan_name(1, 32, 4096, 4096) == "dec_32x64:k8"
+    assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k2"
+    # 33 rows re-read a 32 MiB W twice: the 128-row split tile takes over
+    assert lf.plan_name(1, 33, 4096, 4096) == "dma_128x128x64_s4_g2:k8"
+    assert lf.plan_name(1, 128, 2048, 2048) == "dec_32x64:k4"      # 4 x 8 MiB of W re-reads: still small-M
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
     assert lf.plan_name(2, 2048, 11008, 4104, lf.BF16) == "reg_dual_256x128x64"
@@ -151,7 +155,7 @@ def test_plans(L):
     finally:
         lf.set_plan(None)
     assert lf.plan_name(1, 64, 64, 64) == "dec_32x64"
-    assert lf.plan_name(1, 128, 1024, 1024) == "dec_32x64:k8"   # 4 x 16 tiles, K chunks of 2 steps: 512 workgroups
+    assert lf.plan_name(1, 128, 1024, 1024) == "dec_32x64:k2"   # 4 x 16 tiles, two K chunks of 8 steps
     assert lf.plan_name(1, 129, 4096, 4096) == "dma_128x128x64_s4_g2:k4"  # beyond decode rows
     assert lf.plan_name(2, 1, 256, 4096) == "dma_dual_256x128x32_s4"     # the dual GEMM has no small-M kernel
     # forced split counts
