@@ -157,11 +157,12 @@ Choice choose(const Problem& p) {
         if (t256 >= 224) {
             pl = (p.K % 32 == 0) ? &kPlans[kDma256] : &kPlans[kReg256];
         } else if (p.K % 64 == 0) {
-            // Outputs too small to fill the chip split K; their splits run
-            // the 8-wave tile, whose second K group keeps twice the LDS
-            // reads in flight.
-            const int s = auto_splits(kPlans[kDma128], p);
-            return {s > 1 ? &kPlans[kDma128G2] : &kPlans[kDma128], s};
+            // The 8-wave tile: its second K group keeps twice the LDS reads
+            // in flight and halves each wave's share of the RMS scaling.
+            // Measured equal or faster than the 4-wave 128x128 tile from
+            // 512 to 2048 rows with and without RMSNorm.  Outputs too small
+            // to fill the chip also split K.
+            pl = &kPlans[kDma128G2];
         } else {
             pl = &kPlans[kReg128];
         }
