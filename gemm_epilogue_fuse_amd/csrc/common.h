@@ -190,9 +190,18 @@ struct TileStore {
     static constexpr int kStageFloats = NB * 32 * SROW;
     static constexpr int kBytes = WM * WN * kStageFloats * 4;
 
-    template <int ACT>
+    // Orders this wave's LDS accesses in program order for the compiler; the
+    // LDS executes one wave's instructions in issue order, and each wave
+    // stages through its own region, so no workgroup barrier is needed.
+    static __device__ __forceinline__ void wave_lds_order() {
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    }
+
+    template <int ACT, bool RES>
     static __device__ __forceinline__ void run_act(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
                                                    const float* rs, int m0, int n0, int wm, int wn) {
+        constexpr int NIT = 32 / RPI;  // read-back steps per 32-row slab
         const int lane = threadIdx.x & 63;
         const int wave = threadIdx.x >> 6;
         const int M = p.M, N = p.N;
@@ -201,7 +210,6 @@ struct TileStore {
         const int er = lane / LPR;
         const int gcol = n0 + wn * TN + ec;
         const bool colok = gcol < N;  // N % 8 == 0: a lane's 8 columns are all in or all out
-        const bool has_res = p.resid != nullptr;
         float bias8[8];
         {
             u32x4 bw = {0u, 0u, 0u, 0u};
@@ -214,6 +222,19 @@ struct TileStore {
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
+            // The slab's residual rows are requested before the staging so
+            // their latency hides behind it.  Each lane reads exactly the
+            // elements it later writes, so Y may be the residual buffer.
+            u32x4 rw[RES ? NIT : 1];
+            if constexpr (RES) {
+#pragma unroll
+                for (int it = 0; it < NIT; ++it) {
+                    const int grow = m0 + wm * TM + i * 32 + it * RPI + er;
+                    rw[it] = u32x4{0u, 0u, 0u, 0u};
+                    if (grow < M && colok)
+                        rw[it] = *reinterpret_cast<const u32x4*>(p.resid + (size_t)grow * N + gcol);
+                }
+            }
 #pragma unroll
             for (int nbi = 0; nbi < NB; ++nbi)
 #pragma unroll
@@ -222,8 +243,9 @@ struct TileStore {
                     for (int r = 0; r < 16; ++r)
                         stg[nbi * 32 * SROW + (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SROW + j * 32 +
                             (lane & 31)] = acc[nbi][i][j][r];
-            __syncthreads();
-            for (int it = 0; it < 32 / RPI; ++it) {
+            wave_lds_order();
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
                 const int rr = it * RPI + er;
                 const int rl = wm * TM + i * 32 + rr;
                 const int grow = m0 + rl;
@@ -238,14 +260,11 @@ struct TileStore {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = silu(v[e] * rsc) * (u[e] * rsc);
                 } else {
-                    u32x4 rw = {0u, 0u, 0u, 0u};
-                    if (has_res && grow < M && colok)
-                        rw = *reinterpret_cast<const u32x4*>(p.resid + (size_t)grow * N + gcol);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         float z = (RMS ? v[e] * rsc : v[e]) + bias8[e];
                         z = apply_act<ACT>(z);
-                        if (has_res) z += (e & 1) ? hi_f32<BF>(rw[e >> 1]) : lo_f32<BF>(rw[e >> 1]);
+                        if constexpr (RES) z += (e & 1) ? hi_f32<BF>(rw[it][e >> 1]) : lo_f32<BF>(rw[it][e >> 1]);
                         v[e] = z;
                     }
                 }
@@ -263,21 +282,30 @@ struct TileStore {
                     }
                 }
             }
-            __syncthreads();
+            wave_lds_order();
+        }
+    }
+
+    template <bool RES>
+    static __device__ __forceinline__ void run_res(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
+                                                   const float* rs, int m0, int n0, int wm, int wn) {
+        switch (p.act) {
+        case 1: run_act<1, RES>(p, acc, stage, rs, m0, n0, wm, wn); break;
+        case 2: run_act<2, RES>(p, acc, stage, rs, m0, n0, wm, wn); break;
+        case 3: run_act<3, RES>(p, acc, stage, rs, m0, n0, wm, wn); break;
+        default: run_act<0, RES>(p, acc, stage, rs, m0, n0, wm, wn); break;
         }
     }
 
     static __device__ __forceinline__ void run(const KArgs& p, f32x16 (&acc)[NB][FM][FN], float* stage,
                                                const float* rs, int m0, int n0, int wm, int wn) {
         if constexpr (NB == 2) {
-            run_act<0>(p, acc, stage, rs, m0, n0, wm, wn);
+            run_act<0, false>(p, acc, stage, rs, m0, n0, wm, wn);
         } else {
-            switch (p.act) {
-            case 1: run_act<1>(p, acc, stage, rs, m0, n0, wm, wn); break;
-            case 2: run_act<2>(p, acc, stage, rs, m0, n0, wm, wn); break;
-            case 3: run_act<3>(p, acc, stage, rs, m0, n0, wm, wn); break;
-            default: run_act<0>(p, acc, stage, rs, m0, n0, wm, wn); break;
-            }
+            if (p.resid != nullptr)
+                run_res<true>(p, acc, stage, rs, m0, n0, wm, wn);
+            else
+                run_res<false>(p, acc, stage, rs, m0, n0, wm, wn);
         }
     }
 };
