@@ -124,6 +124,41 @@ __device__ __forceinline__ u32x4 rms_scale(u32x4 x, u32x4 g, float& ss) {
     return o;
 }
 
+// bf16 scaling of one 8-value A fragment, o = round_bf16(x * gamma) pairwise,
+// and ss += x.x, for the one-slot-ahead path.  Each product is one
+// three-operand dot2 against gamma with the other half masked to zero (exact:
+// the product of two bf16 values fits fp32), which saves the zeroing move the
+// compiler pairs with its two-operand form.  gl/gh hold gamma masked to its
+// low / high halves.  t is scratch that stays live across the whole K loop,
+// so its registers are never operands of matrix-core instructions still in
+// flight; every dot2 result is read at least three instructions after it is
+// written, and so is the running ss.
+__device__ __forceinline__ void rms_scale_bf16_ahead(u32x4& x, const uint32_t (&gl)[4], const uint32_t (&gh)[4],
+                                                     float& ss, float (&t)[8]) {
+    asm volatile(
+        "v_dot2c_f32_bf16 %[ss], %[x0], %[x0]\n\t"
+        "v_dot2_f32_bf16 %[t0], %[x0], %[l0], 0\n\t"
+        "v_dot2_f32_bf16 %[t1], %[x0], %[h0], 0\n\t"
+        "v_dot2_f32_bf16 %[t2], %[x1], %[l1], 0\n\t"
+        "v_dot2c_f32_bf16 %[ss], %[x1], %[x1]\n\t"
+        "v_dot2_f32_bf16 %[t3], %[x1], %[h1], 0\n\t"
+        "v_dot2_f32_bf16 %[t4], %[x2], %[l2], 0\n\t"
+        "v_dot2_f32_bf16 %[t5], %[x2], %[h2], 0\n\t"
+        "v_dot2c_f32_bf16 %[ss], %[x2], %[x2]\n\t"
+        "v_dot2_f32_bf16 %[t6], %[x3], %[l3], 0\n\t"
+        "v_dot2_f32_bf16 %[t7], %[x3], %[h3], 0\n\t"
+        "v_cvt_pk_bf16_f32 %[x0], %[t0], %[t1]\n\t"
+        "v_dot2c_f32_bf16 %[ss], %[x3], %[x3]\n\t"
+        "v_cvt_pk_bf16_f32 %[x1], %[t2], %[t3]\n\t"
+        "v_cvt_pk_bf16_f32 %[x2], %[t4], %[t5]\n\t"
+        "v_cvt_pk_bf16_f32 %[x3], %[t6], %[t7]"
+        : [x0] "+v"(x[0]), [x1] "+v"(x[1]), [x2] "+v"(x[2]), [x3] "+v"(x[3]), [ss] "+v"(ss), [t0] "+v"(t[0]),
+          [t1] "+v"(t[1]), [t2] "+v"(t[2]), [t3] "+v"(t[3]), [t4] "+v"(t[4]), [t5] "+v"(t[5]), [t6] "+v"(t[6]),
+          [t7] "+v"(t[7])
+        : [l0] "v"(gl[0]), [l1] "v"(gl[1]), [l2] "v"(gl[2]), [l3] "v"(gl[3]), [h0] "v"(gh[0]), [h1] "v"(gh[1]),
+          [h2] "v"(gh[2]), [h3] "v"(gh[3]));
+}
+
 // The workgroup is KG groups of WM x WN waves.  Group g computes the whole
 // BM x BN tile over its own share of every K step (16-wide sub-steps
 // g*KSG .. g*KSG+KSG-1 of each stage), so KG = 2 doubles the waves that keep
@@ -264,11 +299,18 @@ gemm_dma_kernel(const KArgs p) {
     // A blocks and gamma come first, so they can be scaled early.
     constexpr int NRB = 2 * NB * FN;  // transposing reads per sub-step
     constexpr int G0 = RMS ? 1 : 0;
+    // With sub-step read-ahead and enough matrix-core slots per sub-step,
+    // the next sub-step's A blocks and gamma are read first and scaled a
+    // few slots later, while this sub-step's matrix-core work runs, so no
+    // matrix-core instruction waits on the scaling.  AHEAD_SLOT is the slot
+    // that scales them.
+    constexpr int AHEAD_SLOT = FM + G0 + 2;
+    constexpr bool AHEAD = RMS && !SRA && AHEAD_SLOT < NMMA;
     auto read_piece = [&](Frags& f, int s, int ls, int h, int r) {
         const int ks = g * KSG + ls;
         const int sbase = s * STAGE;
         const int lc = 2 * ks + (lane >> 5);
-        if (SRA) {
+        if (SRA || AHEAD) {
             // order: A0, gamma, A1..A(FM-1), B pieces -> map to the other order's numbering
             if (r >= 1 + G0 && r < G0 + FM) r = r - G0 - 1 + 1 + G0 + NRB;          // A1..
             else if (r >= G0 + FM) r = r - (G0 + FM) + 1 + G0;                      // B pieces
@@ -297,7 +339,7 @@ gemm_dma_kernel(const KArgs p) {
     // (see below).
     auto mma = [&](Frags& cur, int h, int m) {
         const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
-        if constexpr (RMS && !SRA)
+        if constexpr (RMS && !SRA && !AHEAD)
             if (o == 0 && j == 0) cur.a[h][i] = rms_scale<BF>(cur.a[h][i], cur.g[h], ss[i]);
         acc[o][i][j] = mfma32<BF>(cur.a[h][i], cur.b[h][o][j], acc[o][i][j]);
     };
@@ -390,6 +432,14 @@ gemm_dma_kernel(const KArgs p) {
         issue(NS - 1, kstep(NS - 1));
 #pragma unroll
         for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, 0, r);
+        if constexpr (AHEAD) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) F0.a[0][i] = rms_scale<BF>(F0.a[0][i], F0.g[0], ss[i]);
+        }
+        // scratch of the bf16 one-slot-ahead scaling, live across the loop
+        float sct[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sct[q] = 0.0f;
         // Local sub-step s of step kt computes from set s%2.  Its
         // matrix-core instructions are interleaved one by one with the LDS
         // reads of the next local sub-step and with DMA rows.  On the last
@@ -423,6 +473,24 @@ gemm_dma_kernel(const KArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (do_read)
                     if (m < NREAD) read_piece(nxt, rs_stage, rs_ls, 0, m);
+                if constexpr (AHEAD && do_read)
+                    if (m == AHEAD_SLOT) {
+                        // all blocks in one slot: independent chains the
+                        // scheduler can interleave
+                        if constexpr (BF) {
+                            uint32_t gl[4], gh[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                gl[q] = nxt.g[0][q] & 0xffffu;
+                                gh[q] = nxt.g[0][q] & 0xffff0000u;
+                            }
+#pragma unroll
+                            for (int i = 0; i < FM; ++i) rms_scale_bf16_ahead(nxt.a[0][i], gl, gh, ss[i], sct);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < FM; ++i) nxt.a[0][i] = rms_scale<BF>(nxt.a[0][i], nxt.g[0], ss[i]);
+                        }
+                    }
                 if constexpr (do_dma) {
 #pragma unroll
                     for (int d = 0; d < LPT; ++d)
