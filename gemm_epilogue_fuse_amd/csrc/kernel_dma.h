@@ -375,6 +375,10 @@ gemm_dma_kernel(const KArgs p) {
         // path.  FINAL marks the last step, so the steady-state steps carry
         // no conditions at all.
         constexpr int RT = KSG * NREAD;  // fragment reads per step
+        // scratch of the bf16 scaling, live across the loop
+        float sct[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sct[q] = 0.0f;
         auto step = [&](Frags& cur, Frags& nxt, int kt, auto FINAL) {
             constexpr bool fin = decltype(FINAL)::value;
             if constexpr (!fin) {
@@ -386,6 +390,7 @@ gemm_dma_kernel(const KArgs p) {
             const int k_dma = kstep(kt + NS - 1);
 #pragma unroll
             for (int ls = 0; ls < KSG; ++ls) {
+                uint32_t gl[4], gh[4];  // gamma of the following sub-step, masked to each half
 #pragma unroll
                 for (int m = 0; m < NMMA; ++m) {
                     mma(cur, ls, m);
@@ -402,9 +407,21 @@ gemm_dma_kernel(const KArgs p) {
                     if constexpr (RMS) {
                         // block i of the following sub-step at slot NMMA-FM+i
                         const int i = m - (NMMA - FM);
-                        if (i >= 0) {
-                            if (ls + 1 < KSG) cur.a[ls + 1][i] = rms_scale<BF>(cur.a[ls + 1][i], cur.g[ls + 1], ss[i]);
-                            else if (!fin) nxt.a[0][i] = rms_scale<BF>(nxt.a[0][i], nxt.g[0], ss[i]);
+                        if (i >= 0 && (ls + 1 < KSG || !fin)) {
+                            Frags& f = (ls + 1 < KSG) ? cur : nxt;
+                            const int h = (ls + 1 < KSG) ? ls + 1 : 0;
+                            if constexpr (BF) {
+                                if (i == 0) {
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) {
+                                        gl[q] = f.g[h][q] & 0xffffu;
+                                        gh[q] = f.g[h][q] & 0xffff0000u;
+                                    }
+                                }
+                                rms_scale_bf16_ahead(f.a[h][i], gl, gh, ss[i], sct);
+                            } else {
+                                f.a[h][i] = rms_scale<BF>(f.a[h][i], f.g[h], ss[i]);
+                            }
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
