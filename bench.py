@@ -38,7 +38,10 @@ PAGE_A30_MS = 0.208
 
 # Every device source compiled into libfuse: the stored HBM-traffic counters
 # are used only while these hash to the value recorded with them.
-KERNEL_SOURCES = ["gemm_epilogue_fuse_amd/csrc/gemm_fused.hip", "gemm_epilogue_fuse_amd/csrc/kernel_dma.h",
+KERNEL_SOURCES = ["gemm_epilogue_fuse_amd/csrc/gemm_fused.hip", "gemm_epilogue_fuse_amd/csrc/kernels.h",
+                  "gemm_epilogue_fuse_amd/csrc/k_dma_square.hip", "gemm_epilogue_fuse_amd/csrc/k_dma_wide.hip",
+                  "gemm_epilogue_fuse_amd/csrc/k_reg.hip", "gemm_epilogue_fuse_amd/csrc/k_small.hip",
+                  "gemm_epilogue_fuse_amd/csrc/kernel_dma.h",
                   "gemm_epilogue_fuse_amd/csrc/kernel_reg.h", "gemm_epilogue_fuse_amd/csrc/common.h",
                   "gemm_epilogue_fuse_amd/csrc/kernel_decode.h", "gemm_epilogue_fuse_amd/csrc/kernel_strip.h",
                   "gemm_epilogue_fuse_amd/csrc/launch.h"]
@@ -58,12 +61,25 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- timing
 
-def time_calls(fn_for_set, nsets, steps, warmup):
-    """Run fn_for_set(i % nsets) warmup + steps times.  Returns (wall ms/step,
-    device ms per launch): HIP events on the launching stream bracket the
-    whole batch of back-to-back launches, so short kernels are not charged
-    for the host's gap between calls."""
+# Untimed launches before the warmup steps, long enough for the GPU clocks to
+# leave their idle state (a few ms of launches after an idle host phase
+# measured about 10% slow).
+SETTLE_S = 0.3
+
+
+def time_calls(fn_for_set, nsets, steps, warmup, settle_s=SETTLE_S):
+    """Run fn_for_set(i % nsets) for settle_s seconds, then warmup + steps
+    times.  Returns (wall ms/step, device ms per launch): HIP events on the
+    launching stream bracket the whole batch of back-to-back launches, so
+    short kernels are not charged for the host's gap between calls."""
     import torch
+    t_end = time.perf_counter() + settle_s
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(16):
+            fn_for_set(i % nsets)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         fn_for_set(i % nsets)
     torch.cuda.synchronize()
@@ -342,7 +358,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "rmsnorm_linear_512x4096x4096_fp16", "M": M, "K": D, "N": N, "eps": EPS,
                    "bias": None, "act": "none", "seed": 0, "plan": plan, "rotating_input_sets": len(sets),
-                   "parallelism": "none (1 GPU)"},
+                   "clock_settle_s": SETTLE_S, "parallelism": "none (1 GPU)"},
         "latency_us": fields["latency_us"],
         "hbm_gbs": fields["hbm_gbs"],
         "mfma_frac": fields["mfma_frac"],

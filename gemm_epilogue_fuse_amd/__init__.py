@@ -200,7 +200,8 @@ def plan_name(op: int, M: int, N: int, K: int, dtype: int = F16) -> str:
 
 
 def set_plan(name):
-    """Force a single-GEMM tile plan by name (None restores the automatic choice)."""
+    """Force a tile plan by name, "<plan>" or "<plan>:k<S>" (None or "" restores the automatic
+    choice); it applies to the calls it fits, the automatic choice to the others."""
     rc = lib().fuse_set_plan(None if name is None else name.encode())
     if rc != 0:
         raise FuseError(rc, "fuse_set_plan")

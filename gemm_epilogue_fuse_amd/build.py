@@ -17,8 +17,9 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libfuse.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm_fused.hip", "fuse_api.cpp"]
-HEADERS = ["launch.h"]
+# One unit per kernel family, so the units compile in parallel.
+SOURCES = ["gemm_fused.hip", "k_dma_square.hip", "k_dma_wide.hip", "k_reg.hip", "k_small.hip", "fuse_api.cpp"]
+HEADERS = ["launch.h", "kernels.h"]
 
 # Packed-fp32 VALU forms are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -36,7 +37,7 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
+    objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         cmd = [cc, "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I" + INCLUDE, "-I" + CSRC,
@@ -46,10 +47,15 @@ def build(verbose: bool = False) -> str:
         cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError("hipcc failed on %s:\n%s" % (src, r.stderr))
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        _, err = pr.communicate()
+        if pr.returncode != 0:
+            failed.append("hipcc failed on %s:\n%s" % (src, err))
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [cc, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:

@@ -198,11 +198,13 @@ gemm_dma_kernel(const KArgs p) {
     static_assert(SRA || KSG % 2 == 0, "sub-step read-ahead alternates fragment sets within a step");
     static_assert(WIN >= LPT, "one DMA row per matrix-core slot at most");
     using Store = TileStore<BM, BN, WM * KG, WN, BF, RMS, NB>;
-    static_assert(Store::kBytes <= NS * STAGE, "epilogue staging must fit in the LDS stages");
+    // The epilogue staging reuses the stages' LDS, extended where it needs more.
+    constexpr int SMEM_MAIN = (Store::kBytes > NS * STAGE) ? Store::kBytes : NS * STAGE;
+    static_assert(SMEM_MAIN + BM * 4 <= 160 * 1024, "LDS per workgroup");
     static_assert(KG == 1 || KG * NWT * FMO * (NB * FN * 16 + 1) * 64 * 4 <= NS * STAGE,
                   "group reduction must fit in the LDS stages");
 
-    __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + BM * 4];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM_MAIN + BM * 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -714,7 +716,7 @@ gemm_dma_kernel(const KArgs p) {
         if (tid == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    float* rs = reinterpret_cast<float*>(smem + NS * STAGE);
+    float* rs = reinterpret_cast<float*>(smem + SMEM_MAIN);
     if constexpr (RMS) {
         // lanes l and l+32 hold the two k-halves of row l%32 of each block
 #pragma unroll

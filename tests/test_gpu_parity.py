@@ -27,7 +27,11 @@ PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x12
          "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
          "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
          "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
-         "strip_16x16", "strip_32x16"]
+         "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
+         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2"]
+# Gate/up dual-GEMM plans ("" = automatic choice); a forced DMA plan applies where K
+# is a multiple of its K step, the automatic choice elsewhere.
+DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]
 
 
 def fitk(plan, K):
@@ -126,10 +130,17 @@ def test_rmsnorm_gemm_ragged(plan, dtype, act):
             check_bf16_output(out16, out32, want, act)
 
 
+@pytest.fixture(params=DUAL_PLANS)
+def dual_plan(request):
+    lf.set_plan(request.param)
+    yield request.param
+    lf.set_plan(None)
+
+
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 @pytest.mark.parametrize("M,F,K", [(300, 392, 328), (64, 136, 1000), (513, 264, 72), (300, 392, 320),
                                    (513, 264, 1024)])
-def test_swiglu_ragged(dtype, M, F, K):
+def test_swiglu_ragged(dual_plan, dtype, M, F, K):
     T = torch()
     say("swiglu-ragged", dtype, M, F, K, lf.plan_name(2, M, F, K))
     d = synth.swiglu_ffn(M=M, D=K, F=F, seed=24, dtype=dtype)

@@ -23,7 +23,9 @@ PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x12
          "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
          "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
          "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
-         "strip_16x16", "strip_32x16"]
+         "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
+         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2"]
+DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]
 
 
 def fitk(plan, K):
@@ -191,9 +193,16 @@ def test_rmsnorm_unit_rms(plan, dtype):
     assert np.max(np.abs(rms_out - np.sqrt(ms / (ms + 1e-6)))) < tol
 
 
+@pytest.fixture(params=DUAL_PLANS)
+def dual_plan(request):
+    lf.set_plan(request.param)
+    yield request.param
+    lf.set_plan(None)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("K", [264, 320])
-def test_swiglu_plumbing(dtype, K):
+def test_swiglu_plumbing(dual_plan, dtype, K):
     import torch
     # Wg = Wu = I, gamma = 1, rows +-1, eps = 0: H = silu(x) * x exactly per element
     # (K = 264 runs the register-staged plan, K = 320 the DMA plan)
@@ -252,7 +261,7 @@ def test_deterministic(plan_name, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_deterministic_swiglu(dtype):
+def test_deterministic_swiglu(dual_plan, dtype):
     """The gate/up kernel scales A one sub-step ahead with hand-scheduled bf16
     code; repeated calls agree bit for bit (no value read before it lands)."""
     import torch
