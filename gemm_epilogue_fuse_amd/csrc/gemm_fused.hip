@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "kernel_strip.h"
+#include "kernel_wstrip.h"
 #include "kernels.h"
 
 namespace lf {
@@ -40,7 +41,7 @@ namespace {
 
 using dev::KArgs;
 
-enum class Kind { Reg, Dma, Dec, Strip };
+enum class Kind { Reg, Dma, Dec, Strip, WStrip };
 
 // A tile plan: kernel family, tile sizes, K step, LDS stages, wave grid
 // (wm x wn waves, kg K groups; the register-staged kernel always uses 2x2x1),
@@ -70,6 +71,8 @@ constexpr Plan kPlans[] = {
     {"strip_32x16", Kind::Strip, 32, 16, 128, 11, 1, 1, 4, false, false},
     {"dma_256x128x32_s6_w8", Kind::Dma, 256, 128, 32, 6, 4, 2, 1, false, true},
     {"dma_256x128x64_s3_w8", Kind::Dma, 256, 128, 64, 3, 4, 2, 1, false, true},
+    {"wstrip_16x16", Kind::WStrip, 16, 16, 256, 0, 1, 1, 8, false, false},
+    {"wstrip_32x16", Kind::WStrip, 32, 16, 256, 0, 1, 1, 8, false, false},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 static_assert(kNumPlans == kNumPlanIndices, "plan table and PlanIndex (kernels.h) agree");
@@ -82,6 +85,7 @@ bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
     if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
     if (pl.kind == Kind::Strip && p.op != Op::GemmEpilogue && p.K > dev::kStripMaxK) return false;
+    if (pl.kind == Kind::WStrip && p.K > dev::kWStripMaxK) return false;
     return true;
 }
 
@@ -138,10 +142,14 @@ Choice choose(const Problem& p) {
         return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
     }
     const Plan* pl;
-    if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kStrip16], p)) {
+    if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
         // a few rows and a short K: one workgroup per 16-column strip over
-        // all of K (no partial sums cross the device); longer K walks too
-        // many steps per workgroup and splits K instead
+        // all of K (no partial sums cross the device), the whole strip in
+        // flight at once (1024x1024: 4.8 us against 6.0 us for the LDS-ring
+        // strip).  At longer K the 16-column strips read a quarter of each
+        // 128-byte line per workgroup and lose to 64-column tiles with split K.
+        pl = &kPlans[kWStrip16];
+    } else if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kStrip16], p)) {
         pl = &kPlans[kStrip16];
     } else if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0 &&
                ((p.M + 31) / 32) * p.K * p.N * 2 <= kDecodeMaxWBytes) {
@@ -228,7 +236,8 @@ const void* kernel_for(int pi, const Problem& p, bool split) {
     switch (kPlans[pi].kind) {
     case Kind::Reg: return kernels_reg(s);
     case Kind::Dec:
-    case Kind::Strip: return kernels_small(s);
+    case Kind::Strip:
+    case Kind::WStrip: return kernels_small(s);
     case Kind::Dma: return (kPlans[pi].bm == kPlans[pi].bn) ? kernels_dma_square(s) : kernels_dma_wide(s);
     }
     return nullptr;
@@ -290,7 +299,7 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     a.K = (int)p.K;
     a.tiles_m = (int)((p.M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((p.N + pl.bn - 1) / pl.bn);
-    a.group_m = (pl.kind == Kind::Dec || pl.kind == Kind::Strip) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
+    a.group_m = (pl.kind == Kind::Dec || pl.kind == Kind::Strip || pl.kind == Kind::WStrip) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
     a.act = p.act;
     a.out_f32 = p.out_f32 ? 1 : 0;
     a.eps = p.eps;

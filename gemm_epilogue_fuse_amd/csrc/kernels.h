@@ -22,7 +22,9 @@ enum PlanIndex : int {
     kStrip32 = 11,
     kDma256x128W8 = 12,
     kDma256x128x64W8 = 13,
-    kNumPlanIndices = 14
+    kWStrip16 = 14,
+    kWStrip32 = 15,
+    kNumPlanIndices = 16
 };
 
 // Which instantiation of a plan's kernel a call needs.

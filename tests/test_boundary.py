@@ -135,8 +135,9 @@ def test_plans(L):
     assert lf.plan_name(0, 2048, 4096, 11008, lf.BF16) == "dma_256x128x64_s3_w8"  # the SwiGLU down GEMM
     assert lf.plan_name(0, 1024, 4096, 4096) == "dma_128x128x64_s4_g2"  # 256 tiles of 128^2: 8-wave K-group tile
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
-    assert lf.plan_name(1, 1, 1024, 1024) == "strip_16x16"      # decode, a few rows, short K: column strips over all of K
-    assert lf.plan_name(1, 32, 1024, 1024, lf.BF16) == "strip_16x16"  # two row tiles of 16 still beat one of 32
+    assert lf.plan_name(1, 1, 1024, 1024) == "wstrip_16x16"     # decode, a few rows, short K: column strips over all of K
+    assert lf.plan_name(1, 32, 1024, 1024, lf.BF16) == "wstrip_16x16"  # two row tiles of 16 still beat one of 32
+    assert lf.plan_name(1, 8, 1024, 896) == "strip_16x16"       # K % 256 != 0: the LDS-ring strip
     assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, K chunks of 8 steps
     assert lf.plan_name(1, 32, 4096, 4096) == "dec_32x64:k8"
     assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k2"

@@ -28,18 +28,20 @@ PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x12
          "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
          "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
          "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
-         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2"]
+         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2", "wstrip_16x16", "wstrip_32x16"]
 # Gate/up dual-GEMM plans ("" = automatic choice); a forced DMA plan applies where K
 # is a multiple of its K step, the automatic choice elsewhere.
 DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]
 
 
 def fitk(plan, K):
-    """DMA and small-M plans need K % 64 == 0 (strips K % 128): round K up for them (M and N stay ragged);
+    """DMA and small-M plans need K % 64 == 0 (strips K % 128, whole strips K % 256): round K up for them
+    (M and N stay ragged);
     split plans get at least 3 K steps per split."""
-    if not plan.startswith(("dma", "dec", "strip")):
+    if not plan.startswith(("dma", "dec", "strip", "wstrip")):
         return K
-    K = -(-K // (128 if plan.startswith("strip") else 64)) * (128 if plan.startswith("strip") else 64)
+    step = 256 if plan.startswith("wstrip") else 128 if plan.startswith("strip") else 64
+    K = -(-K // step) * step
     if plan.startswith("dec") and ":k" not in plan:
         K = min(K, 512)  # one K chunk: at most 8 steps of 64
     if ":k" in plan:
@@ -165,6 +167,35 @@ def test_small_workload_gemm_bias_gelu():
     want = oracle.gemm_epilogue(x["A"], x["W"], x["bias"], None, "gelu_tanh")
     got = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], None, "gelu_tanh"))
     assert_close(got, want, "C1")
+
+
+@pytest.mark.parametrize("wplan", ["wstrip_16x16", "wstrip_32x16"])
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("M,N,K", [(1, 264, 1280), (5, 136, 2048), (17, 520, 3072), (32, 4104, 4096)])
+def test_whole_strip_long_k(wplan, dtype, M, N, K):
+    """The whole-strip kernels at 5..16 blocks of 32 k per wave (K = 1280..4096),
+    where the padded block counts 8 and 16 are used; N % 16 == 8 leaves half of
+    the last strip outside the output."""
+    T = torch()
+    lf.set_plan(wplan)
+    try:
+        assert lf.plan_name(1, M, N, K) == wplan
+        say("whole-strip", wplan, dtype, M, N, K)
+        d = synth.rmsnorm_linear(M=M, D=K, N=N, seed=25, dtype=dtype)
+        g = synth.generator(26)
+        b = synth.to_bits(g.standard_normal(N) * 0.1, dtype)
+        R = synth.to_bits(g.standard_normal((M, N)), dtype)
+        t = {k: dev_t(v, dtype) for k, v in d.items()}
+        x = w64(d, dtype)
+        want = oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["W"], synth.widen(b, dtype), "gelu_tanh")
+        out32 = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, dev_t(b, dtype), "gelu_tanh",
+                                     out_dtype=T.float32))
+        assert_close(out32, want, "rms gelu f32out")
+        want = oracle.gemm_epilogue(x["X"], x["W"], synth.widen(b, dtype), synth.widen(R, dtype), "silu")
+        out32 = to64(lf.gemm_epilogue(t["X"], t["W"], dev_t(b, dtype), dev_t(R, dtype), "silu", out_dtype=T.float32))
+        assert_close(out32, want, "gemm silu residual f32out")
+    finally:
+        lf.set_plan(None)
 
 
 # --------------------------------------------------------------------------- full sizes (automatic plan)
