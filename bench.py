@@ -67,13 +67,13 @@ def log(*a):
 SETTLE_S = 0.3
 
 
-def time_calls(fn_for_set, nsets, steps, warmup, settle_s=SETTLE_S):
+def time_calls(fn_for_set, nsets, steps, warmup, settle_s=None):
     """Run fn_for_set(i % nsets) for settle_s seconds, then warmup + steps
     times.  Returns (wall ms/step, device ms per launch): HIP events on the
     launching stream bracket the whole batch of back-to-back launches, so
     short kernels are not charged for the host's gap between calls."""
     import torch
-    t_end = time.perf_counter() + settle_s
+    t_end = time.perf_counter() + (SETTLE_S if settle_s is None else settle_s)
     i = 0
     while time.perf_counter() < t_end:
         for _ in range(16):
@@ -304,6 +304,7 @@ def sweep(steps, warmup):
 # ----------------------------------------------------------------------------- main
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -311,7 +312,10 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed launches before the warmup steps (0 under counter runs)")
     args = ap.parse_args()
+    SETTLE_S = max(0.0, args.settle)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs the fused kernels on a single MI355X "
