@@ -95,11 +95,14 @@ def time_calls(fn_for_set, nsets, steps, warmup, settle_s=None):
     return wall_ms, dev_ms
 
 
-def launch_floor_us(steps=200):
+def launch_floor_us(steps=200, graph=False):
     """Device time per launch of a one-element device op, timed like the
-    kernels: the floor under any call's latency."""
+    kernels (eager, or by HIP-graph replay): the floor under any call's
+    latency."""
     import torch
     x = torch.zeros(1, device="cuda:0")
+    if graph:
+        return round(graph_time_ms(lambda i, strm: x.add_(1.0), 1) * 1e3, 3)
     _, dev = time_calls(lambda i: x.add_(1.0), 1, steps, 20)
     return round(dev * 1e3, 3)
 
@@ -133,7 +136,7 @@ def torch_empty(shape, dtype):
     return torch.empty(shape, dtype=dtype, device="cuda:0")
 
 
-def bench_rms_linear(M, D, N, dtype_s, steps, warmup, order=("X", "gamma", "W")):
+def bench_rms_linear(M, D, N, dtype_s, steps, warmup, order=("X", "gamma", "W"), graph=False):
     """Time fuse_rmsnorm_gemm through the C ABI with pre-marshalled pointers
     (what a native caller does), so host-side Python cost stays out of the way."""
     import ctypes
@@ -147,15 +150,50 @@ def bench_rms_linear(M, D, N, dtype_s, steps, warmup, order=("X", "gamma", "W"))
     argv = [(s["X"].data_ptr(), s["gamma"].data_ptr(), s["W"].data_ptr(), s["Y"].data_ptr()) for s in sets]
     fn = L.fuse_rmsnorm_gemm
 
-    def call(i):
+    def call_on(i, strm):
         x, g, w, y = argv[i]
-        rc = fn(x, g, eps, w, None, y, M, N, D, 0, code, stream)
+        rc = fn(x, g, eps, w, None, y, M, N, D, 0, code, strm)
         if rc:
             raise lf.FuseError(rc, "fuse_rmsnorm_gemm")
+
+    def call(i):
+        call_on(i, stream)
     wall, dev = time_calls(call, len(sets), steps, warmup)
     flops = 2.0 * M * N * D
     alg_bytes = (M * D + D + D * N + M * N) * 2
+    if graph:
+        gdev = graph_time_ms(call_on, len(sets))
+        return d, sets, wall, dev, flops, alg_bytes, gdev
     return d, sets, wall, dev, flops, alg_bytes
+
+
+def graph_time_ms(call_on, nsets, launches=40, replays=10):
+    """Device ms per launch from a HIP graph of `launches` back-to-back calls
+    over the rotating input sets, replayed `replays` times: no host launch
+    gap between kernels, so short calls show their device time."""
+    import ctypes
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    sp = ctypes.c_void_p(s.cuda_stream)
+    with torch.cuda.stream(s):
+        for i in range(nsets):  # per-stream library state (split-K workspace) exists before capture
+            call_on(i, sp)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(launches):
+            call_on(i % nsets, sp)
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+    s.synchronize()
+    return e0.elapsed_time(e1) / (launches * replays)
 
 
 def result_fields(dev_ms, flops, alg_bytes):
@@ -283,18 +321,23 @@ def sweep(steps, warmup):
     emit(r3)
     del t, H, Y
 
-    # decode-shaped RMSNorm -> Linear; cells whose roofline time is under the
-    # launch floor cannot show their HBM fraction and are flagged
-    floor = launch_floor_us()
-    emit({"workload": "launch_floor_one_element_op", "latency_us": floor})
+    # decode-shaped RMSNorm -> Linear, timed by HIP-graph replay (eager
+    # launches of a few-microsecond kernel measure the host's launch rate);
+    # cells whose roofline time is under the launch floor cannot show their
+    # HBM fraction and are flagged
+    floor = launch_floor_us(graph=True)
+    emit({"workload": "launch_floor_one_element_op", "latency_us": floor, "timing": "HIP graph of 40 launches, replayed",
+          "eager_latency_us": launch_floor_us()})
     for dt in (synth.F16, synth.BF16):
         for D in (1024, 2048, 4096):
             for B in (1, 32, 128, 512, 1024):
-                _, sets, _, dev, flops, alg = bench_rms_linear(B, D, D, dt, steps, warmup,
-                                                               order=("W", "X", "gamma"))
+                _, sets, _, dev, flops, alg, gdev = bench_rms_linear(B, D, D, dt, steps, warmup,
+                                                                     order=("W", "X", "gamma"), graph=True)
                 rec = {"workload": "decode_rmsnorm_linear_B%d_D%d_%s" % (B, D, dt),
-                       "plan": lf.plan_name(1, B, D, D, lf.BF16 if dt == synth.BF16 else lf.F16)}
-                rec.update(result_fields(dev, flops, alg))
+                       "plan": lf.plan_name(1, B, D, D, lf.BF16 if dt == synth.BF16 else lf.F16),
+                       "timing": "HIP graph of 40 launches, replayed"}
+                rec.update(result_fields(gdev, flops, alg))
+                rec["eager_latency_us"] = round(dev * 1e3, 3)
                 rec["launch_floor_us"] = floor
                 rec["below_launch_floor"] = rec["roof_us"] < floor
                 emit(rec)

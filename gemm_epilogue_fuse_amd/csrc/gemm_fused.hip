@@ -73,6 +73,7 @@ constexpr Plan kPlans[] = {
     {"dma_256x128x64_s3_w8", Kind::Dma, 256, 128, 64, 3, 4, 2, 1, false, true},
     {"wstrip_16x16", Kind::WStrip, 16, 16, 256, 0, 1, 1, 8, false, false},
     {"wstrip_32x16", Kind::WStrip, 32, 16, 256, 0, 1, 1, 8, false, false},
+    {"dma_64x128x64_s4_g2", Kind::Dma, 64, 128, 64, 4, 1, 2, 2, false, true},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 static_assert(kNumPlans == kNumPlanIndices, "plan table and PlanIndex (kernels.h) agree");
@@ -175,6 +176,13 @@ Choice choose(const Problem& p) {
             // 512 to 2048 rows with and without RMSNorm.  Outputs too small
             // to fill the chip also split K.
             pl = &kPlans[kDma128G2];
+            // Exchanging 128x128 fp32 partials pays off only when each split
+            // keeps at least 32 K steps; with shorter splits the 64x128 tile
+            // (twice the tiles, half the partial per tile, fewer splits) is
+            // faster: 128x4096x4096 22.8 -> 18.2 us, 512x2048x2048 18.1 ->
+            // 15.3 us, 512x1024x1024 12.3 -> 9.8 us.
+            const int s128 = auto_splits(*pl, p);
+            if (s128 > 1 && p.K / 64 / s128 < 32) pl = &kPlans[kDma64x128G2];
         } else {
             pl = &kPlans[kReg128];
         }

@@ -1,9 +1,10 @@
-// k_dma_wide.hip -- instantiations of the LDS-DMA kernel for 256x128 tiles:
+// k_dma_wide.hip -- instantiations of the LDS-DMA kernel for non-square tiles:
 // the single GEMM with 8 waves as 4 x 2, 64x64 per wave (a 32-wide K step in
 // 6 stages with whole-step fragment read-ahead, or a 64-wide step in 3 stages
 // with sub-step read-ahead, which keeps a 64x64 wave within its registers),
-// with and without the split-K exchange; and the SwiGLU gate/up dual GEMM
-// (4 waves, two accumulator sets sharing the A tile).
+// with and without the split-K exchange; the 64x128 tile with 4 waves in two K
+// groups of 1 x 2 (64x64 per wave); and the SwiGLU gate/up dual GEMM (4 waves,
+// two accumulator sets sharing the A tile).
 #include "kernels.h"
 #include "kernel_dma.h"
 
@@ -20,6 +21,9 @@ const void* wide(const KernelSel& s) {
     case kDma256x128x64W8:
         return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, RMS, 1, true>)
                        : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, RMS, 1, false>);
+    case kDma64x128G2:
+        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, RMS, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, RMS, 1, false>);
     case kDual:
         if constexpr (RMS)
             return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 4, 2, 2, 1, false, BF, true, 2, false>);

@@ -24,7 +24,8 @@ enum PlanIndex : int {
     kDma256x128x64W8 = 13,
     kWStrip16 = 14,
     kWStrip32 = 15,
-    kNumPlanIndices = 16
+    kDma64x128G2 = 16,
+    kNumPlanIndices = 17
 };
 
 // Which instantiation of a plan's kernel a call needs.
@@ -39,7 +40,7 @@ struct KernelSel {
 // Host-side kernel handles for hipLaunchKernel, or nullptr when the unit
 // holds no kernel for `s`.
 const void* kernels_dma_square(const KernelSel& s);  // k_dma_square.hip: 128x128 and 256x256 tiles
-const void* kernels_dma_wide(const KernelSel& s);    // k_dma_wide.hip: 256x128 tiles, dual gate/up
+const void* kernels_dma_wide(const KernelSel& s);    // k_dma_wide.hip: 256x128 and 64x128 tiles, dual gate/up
 const void* kernels_reg(const KernelSel& s);         // k_reg.hip: register-staged tiles
 const void* kernels_small(const KernelSel& s);       // k_small.hip: small-M and strip kernels
 

@@ -141,8 +141,12 @@ def test_plans(L):
     assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, K chunks of 8 steps
     assert lf.plan_name(1, 32, 4096, 4096) == "dec_32x64:k8"
     assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k2"
-    # 33 rows re-read a 32 MiB W twice: the 128-row split tile takes over
-    assert lf.plan_name(1, 33, 4096, 4096) == "dma_128x128x64_s4_g2:k8"
+    # 33 rows re-read a 32 MiB W twice: a split tile takes over; 128x128 would split
+    # K eight ways (8 steps per split), so the 64x128 tile splits it four ways
+    assert lf.plan_name(1, 33, 4096, 4096) == "dma_64x128x64_s4_g2:k8"
+    assert lf.plan_name(1, 128, 4096, 4096) == "dma_64x128x64_s4_g2:k4"
+    assert lf.plan_name(1, 512, 1024, 1024) == "dma_64x128x64_s4_g2:k2"
+    assert lf.plan_name(0, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"  # 32 K steps per split: keeps 128x128
     assert lf.plan_name(1, 128, 2048, 2048) == "dec_32x64:k4"      # 4 x 8 MiB of W re-reads: still small-M
     assert lf.plan_name(1, 512, 4096, 4104) == "reg_128x128x64"      # K % 64 != 0
     assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
@@ -160,7 +164,7 @@ def test_plans(L):
         lf.set_plan(None)
     assert lf.plan_name(1, 64, 64, 64) == "dec_32x64"
     assert lf.plan_name(1, 128, 1024, 1024) == "dec_32x64:k2"   # 4 x 16 tiles, two K chunks of 8 steps
-    assert lf.plan_name(1, 129, 4096, 4096) == "dma_128x128x64_s4_g2:k4"  # beyond decode rows
+    assert lf.plan_name(1, 129, 4096, 4096) == "dma_64x128x64_s4_g2:k2"  # beyond decode rows: 3 x 32 tiles of 64x128
     assert lf.plan_name(2, 1, 256, 4096) == "dma_dual_256x128x32_s4"     # the dual GEMM has no small-M kernel
     # forced split counts
     lf.set_plan("dma_128x128x64_s4:k4")
