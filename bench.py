@@ -299,6 +299,29 @@ def sweep(steps, warmup):
         emit(rec)
         del sets, base
 
+    # The same work unfused through the vendor library, for context: torch's
+    # rms_norm, matmul (hipBLASLt) and elementwise kernels, timed the same way
+    # (warm inputs: one set).
+    def unfused(name, fn, flops, alg):
+        _, dev = time_calls(lambda i: fn(), 1, steps, warmup)
+        rec = {"workload": name, "plan": "torch (hipBLASLt matmul + separate elementwise kernels)"}
+        rec.update(result_fields(dev, flops, alg))
+        emit(rec)
+
+    F = torch.nn.functional
+    X = torch.randn(512, 4096, device="cuda:0").half()
+    g = (1 + 0.1 * torch.randn(4096, device="cuda:0")).half()
+    W = (torch.randn(4096, 4096, device="cuda:0") / 64).half()
+    unfused("unfused_rmsnorm_then_matmul_512x4096x4096_fp16",
+            lambda: torch.matmul(F.rms_norm(X, (4096,), g, EPS), W),
+            2.0 * 512 * 4096 * 4096, (2 * 512 * 4096 + 4096 + 4096 * 4096) * 2)
+    A = torch.randn(4096, 4096, device="cuda:0").half()
+    bias = (0.1 * torch.randn(4096, device="cuda:0")).half()
+    unfused("unfused_matmul_bias_gelu_tanh_4096x4096x4096_fp16",
+            lambda: F.gelu(torch.matmul(A, W) + bias, approximate="tanh"),
+            2.0 * 4096 ** 3, (3 * 4096 * 4096 + 4096) * 2)
+    del X, g, W, A, bias
+
     # SwiGLU FFN block, bf16: kernel 1 (RMSNorm + gate/up + SiLU*up), kernel 2 (down + bias + residual)
     M, D, F = 2048, 4096, 11008
     d = synth.swiglu_ffn(M=M, D=D, F=F, seed=0)

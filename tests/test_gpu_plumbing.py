@@ -277,3 +277,43 @@ def test_deterministic_swiglu(dual_plan, dtype):
         y = lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], 1e-6, out_dtype=torch.float32)
         assert torch.equal(y.view(torch.int32), ref.view(torch.int32))
     assert bool(torch.isfinite(ref).all())
+
+
+@pytest.mark.parametrize("plan_name", ["dma_128x128x64_s4_g2:k2", "dma_64x128x64_s4_g2:k3", "dec_32x64:k3",
+                                       "dma_256x128x64_s3_w8:k2", "wstrip_16x16", "auto-decode"])
+def test_graph_replay_matches_eager(plan_name):
+    """Calls captured in a HIP graph (on a stream that made one eager call
+    first, so its split-K workspace exists) and replayed several times, with
+    eager work between the replays, give the eager result bit for bit: the
+    split-K arrival counters are back at zero after every call."""
+    import torch
+    auto = plan_name == "auto-decode"
+    lf.set_plan(None if auto else plan_name)
+    try:
+        M, D, N = (1, 4096, 4096) if auto else (100, fitk(plan_name, 520), 392)
+        if not auto:
+            assert lf.plan_name(1, M, N, D) == plan_name
+        say("graph replay", plan_name, M, D, N, lf.plan_name(1, M, N, D))
+        d = synth.rmsnorm_linear(M=M, D=D, N=N, seed=4, dtype=synth.F16)
+        t = {k: dev_t(v, synth.F16) for k, v in d.items()}
+        ref = lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], act="silu", out_dtype=torch.float32).clone()
+        outs = [torch.empty((M, N), dtype=torch.float32, device="cuda:0") for _ in range(2)]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], act="silu", out=outs[0], out_dtype=torch.float32)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for o in outs:
+                lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], act="silu", out=o, out_dtype=torch.float32)
+        for _ in range(4):
+            for o in outs:
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for o in outs:
+                assert torch.equal(o.view(torch.int32), ref.view(torch.int32))
+    finally:
+        lf.set_plan(None)
