@@ -265,7 +265,9 @@ def cpu_baseline(min_seconds=10.0):
 
 # ----------------------------------------------------------------------------- sweep
 
-def sweep(steps, warmup):
+def sweep(steps, warmup, only=None):
+    """One JSON line per workload on stderr; `only` keeps the workloads whose
+    name contains it (for profiling one kernel at a time)."""
     import torch
     import gemm_epilogue_fuse_amd as lf
     import synth
@@ -273,11 +275,17 @@ def sweep(steps, warmup):
     def emit(rec):
         print(json.dumps(rec), file=sys.stderr, flush=True)
 
+    def want(name):
+        return only is None or only in name
+
     # GEMM + bias + activation, N = K = 4096
     for M, act, resid in [(512, "gelu_tanh", False), (1024, "gelu_tanh", False), (2048, "gelu_tanh", False),
                           (4096, "gelu_tanh", False), (4096, "silu", False), (4096, "relu", False),
                           (4096, "none", True)]:
         N = K = 4096
+        name = "gemm_bias_%s%s_%dx4096x4096_fp16" % (act, "_residual" if resid else "", M)
+        if not want(name):
+            continue
         d = synth.gemm_epilogue_sweep(M, N, K, seed=0, residual=resid)
         base = {k: synth.to_torch(v, synth.F16, "cuda:0") for k, v in d.items()}
         per = (M * K + K * N + N + M * N * (2 if resid else 1)) * 2
@@ -293,8 +301,7 @@ def sweep(steps, warmup):
             s = sets[i]
             lf.gemm_epilogue(s["A"], s["W"], s["bias"], s.get("R"), act, out=s["Y"])
         _, dev = time_calls(call, len(sets), steps, warmup)
-        rec = {"workload": "gemm_bias_%s%s_%dx4096x4096_fp16" % (act, "_residual" if resid else "", M),
-               "plan": lf.plan_name(0, M, N, K)}
+        rec = {"workload": name, "plan": lf.plan_name(0, M, N, K)}
         rec.update(result_fields(dev, 2.0 * M * N * K, per))
         emit(rec)
         del sets, base
@@ -303,6 +310,8 @@ def sweep(steps, warmup):
     # rms_norm, matmul (hipBLASLt) and elementwise kernels, timed the same way
     # (warm inputs: one set).
     def unfused(name, fn, flops, alg):
+        if not want(name):
+            return
         _, dev = time_calls(lambda i: fn(), 1, steps, warmup)
         rec = {"workload": name, "plan": "torch (hipBLASLt matmul + separate elementwise kernels)"}
         rec.update(result_fields(dev, flops, alg))
@@ -324,6 +333,43 @@ def sweep(steps, warmup):
 
     # SwiGLU FFN block, bf16: kernel 1 (RMSNorm + gate/up + SiLU*up), kernel 2 (down + bias + residual)
     M, D, F = 2048, 4096, 11008
+    n1 = "swiglu_k1_rmsnorm_gate_up_2048x11008x4096_bf16"
+    n2 = "swiglu_k2_down_bias_residual_2048x4096x11008_bf16"
+    n3 = "swiglu_ffn_block_bf16_total"
+    if want(n1) or want(n2) or want(n3):
+        swiglu_block(lf, synth, emit, steps, warmup, M, D, F, n1, n2, n3)
+
+    # decode-shaped RMSNorm -> Linear, timed by HIP-graph replay (eager
+    # launches of a few-microsecond kernel measure the host's launch rate);
+    # cells whose roofline time is under the launch floor cannot show their
+    # HBM fraction and are flagged
+    floor = launch_floor_us(graph=True)
+    if want("launch_floor_one_element_op"):
+        emit({"workload": "launch_floor_one_element_op", "latency_us": floor,
+              "timing": "HIP graph of 40 launches, replayed", "eager_latency_us": launch_floor_us()})
+    for dt in (synth.F16, synth.BF16):
+        for D in (1024, 2048, 4096):
+            for B in (1, 32, 128, 512, 1024):
+                name = "decode_rmsnorm_linear_B%d_D%d_%s" % (B, D, dt)
+                if not want(name):
+                    continue
+                _, sets, _, dev, flops, alg, gdev = bench_rms_linear(B, D, D, dt, steps, warmup,
+                                                                     order=("W", "X", "gamma"), graph=True)
+                rec = {"workload": name,
+                       "plan": lf.plan_name(1, B, D, D, lf.BF16 if dt == synth.BF16 else lf.F16),
+                       "timing": "HIP graph of 40 launches, replayed"}
+                rec.update(result_fields(gdev, flops, alg))
+                rec["eager_latency_us"] = round(dev * 1e3, 3)
+                rec["launch_floor_us"] = floor
+                rec["below_launch_floor"] = rec["roof_us"] < floor
+                emit(rec)
+                del sets
+
+
+def swiglu_block(lf, synth, emit, steps, warmup, M, D, F, n1, n2, n3):
+    """SwiGLU FFN block in bf16: kernel 1 (RMSNorm + gate/up + SiLU*up) and
+    kernel 2 (down + bias + residual)."""
+    import torch
     d = synth.swiglu_ffn(M=M, D=D, F=F, seed=0)
     t = {k: synth.to_torch(v, synth.BF16, "cuda:0") for k, v in d.items()}
     H = torch.empty((M, F), dtype=torch.bfloat16, device="cuda:0")
@@ -333,38 +379,15 @@ def sweep(steps, warmup):
     _, dev2 = time_calls(lambda i: lf.gemm_epilogue(H, t["Wd"], t["bias"], t["X"], "none", out=Y), 1, steps, warmup)
     b1 = (M * D + D + 2 * D * F + M * F) * 2
     b2 = (M * F + F * D + D + 2 * M * D) * 2
-    r1 = {"workload": "swiglu_k1_rmsnorm_gate_up_2048x11008x4096_bf16", "plan": lf.plan_name(2, M, F, D, lf.BF16)}
+    r1 = {"workload": n1, "plan": lf.plan_name(2, M, F, D, lf.BF16)}
     r1.update(result_fields(dev1, 4.0 * M * F * D, b1))
     emit(r1)
-    r2 = {"workload": "swiglu_k2_down_bias_residual_2048x4096x11008_bf16", "plan": lf.plan_name(0, M, D, F, lf.BF16)}
+    r2 = {"workload": n2, "plan": lf.plan_name(0, M, D, F, lf.BF16)}
     r2.update(result_fields(dev2, 2.0 * M * D * F, b2))
     emit(r2)
-    r3 = {"workload": "swiglu_ffn_block_bf16_total"}
+    r3 = {"workload": n3}
     r3.update(result_fields(dev1 + dev2, 4.0 * M * F * D + 2.0 * M * D * F, b1 + b2))
     emit(r3)
-    del t, H, Y
-
-    # decode-shaped RMSNorm -> Linear, timed by HIP-graph replay (eager
-    # launches of a few-microsecond kernel measure the host's launch rate);
-    # cells whose roofline time is under the launch floor cannot show their
-    # HBM fraction and are flagged
-    floor = launch_floor_us(graph=True)
-    emit({"workload": "launch_floor_one_element_op", "latency_us": floor, "timing": "HIP graph of 40 launches, replayed",
-          "eager_latency_us": launch_floor_us()})
-    for dt in (synth.F16, synth.BF16):
-        for D in (1024, 2048, 4096):
-            for B in (1, 32, 128, 512, 1024):
-                _, sets, _, dev, flops, alg, gdev = bench_rms_linear(B, D, D, dt, steps, warmup,
-                                                                     order=("W", "X", "gamma"), graph=True)
-                rec = {"workload": "decode_rmsnorm_linear_B%d_D%d_%s" % (B, D, dt),
-                       "plan": lf.plan_name(1, B, D, D, lf.BF16 if dt == synth.BF16 else lf.F16),
-                       "timing": "HIP graph of 40 launches, replayed"}
-                rec.update(result_fields(gdev, flops, alg))
-                rec["eager_latency_us"] = round(dev * 1e3, 3)
-                rec["launch_floor_us"] = floor
-                rec["below_launch_floor"] = rec["roof_us"] < floor
-                emit(rec)
-                del sets
 
 
 # ----------------------------------------------------------------------------- main
@@ -376,6 +399,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", default=None, help="with --sweep: only the workloads whose name contains this")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
@@ -447,7 +471,7 @@ def main():
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
     if args.sweep:
-        sweep(max(20, args.steps // 4), max(5, args.warmup // 2))
+        sweep(max(20, args.steps // 4), max(5, args.warmup // 2), args.only)
 
 
 if __name__ == "__main__":
