@@ -48,6 +48,17 @@
  *  Alignment   Every pointer 16-byte aligned.
  *  Ownership   All pointers are device memory owned by the caller.  The library
  *              keeps no pointer after the call returns.
+ *  Workspace   Plans that split K across workgroups exchange float32 partial
+ *              sums through a library-owned device buffer, one per (device,
+ *              stream), allocated by the first call on that stream that needs
+ *              it (at least 64 MiB plus 1 MiB of arrival counters) and kept
+ *              until the process ends.  A call that needs a larger buffer
+ *              first synchronises its stream, then frees and reallocates.
+ *              Calls on one stream use it in stream order; calls on
+ *              different streams never share it.  A call captured into a
+ *              HIP graph must come after one eager call of the same size on
+ *              the capturing stream: an allocation during capture fails with
+ *              FUSE_E_HIP.
  *  Stream      `stream` is a hipStream_t (NULL: the default stream).  Calls are
  *              asynchronous: they return once the kernel is enqueued.
  *  Aliasing    Y must not overlap any input, except Y == residual exactly
@@ -137,9 +148,12 @@ int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
  * problem shape.  fuse_plan_name reports the plan a call with these arguments
  * would use (op: 0 = fuse_gemm_epilogue, 1 = fuse_rmsnorm_gemm,
  * 2 = fuse_rmsnorm_gemm_swiglu); it returns "invalid" for an unknown op.
- * fuse_set_plan forces one plan by name for every later single-GEMM call of
- * this process (tuning and testing only; NULL or "" restores the automatic
- * choice) and returns FUSE_E_ENUM for an unknown name.  The override is
+ * fuse_set_plan forces one plan by name, "<plan>" or "<plan>:k<S>" for S-way
+ * split K, for every later call of this process that the plan fits (a
+ * gate/up dual plan only fuse_rmsnorm_gemm_swiglu, the others the two
+ * single-GEMM entry points; a call it does not fit keeps the automatic
+ * choice).  It is for tuning and testing only; NULL or "" restores the
+ * automatic choice, and an unknown name returns FUSE_E_ENUM.  The override is
  * process-wide; calls racing with it see either the old or the new plan.
  */
 const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype);
