@@ -56,9 +56,9 @@
  *              first synchronises its stream, then frees and reallocates.
  *              Calls on one stream use it in stream order; calls on
  *              different streams never share it.  A call captured into a
- *              HIP graph must come after one eager call of the same size on
- *              the capturing stream: an allocation during capture fails with
- *              FUSE_E_HIP.
+ *              HIP graph must come after an eager call on the capturing
+ *              stream that needed at least as much workspace: an allocation
+ *              during capture fails with FUSE_E_HIP.
  *  Stream      `stream` is a hipStream_t (NULL: the default stream).  Calls are
  *              asynchronous: they return once the kernel is enqueued.
  *  Aliasing    Y must not overlap any input, except Y == residual exactly
