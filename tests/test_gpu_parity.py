@@ -291,3 +291,31 @@ def test_decode_rmsnorm_linear_sweep(B, D, dtype):
         assert_close(Y[rows], want, "C5 bf16 f32out")
         Y16 = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS))
         check_bf16_output(Y16[rows], Y[rows], want, "C5")
+
+
+def test_largest_accepted_shape_sampled_rows():
+    """M = 131064, K = N = 4096: M*K is just under the 2^29-element limit of the
+    ABI (A and Y are 1 GiB each in fp16) and the last 256-row tile is ragged.
+    A repeats a seeded 4096-row block, so each sampled row has an oracle value;
+    rows from the first, middle and last tiles are checked, for the GEMM +
+    bias + GeLU and for RMSNorm -> Linear."""
+    T = torch()
+    M, K, N, base_rows = 131064, 4096, 4096, 4096
+    assert M * K < (1 << 29) and (M + 8) * K >= (1 << 29)
+    say("largest shape", M, K, N, lf.plan_name(0, M, N, K), lf.plan_name(1, M, N, K))
+    d = synth.rmsnorm_linear(M=base_rows, D=K, N=N, seed=27)
+    b = synth.to_bits(synth.generator(28).standard_normal(N) * 0.1, synth.F16)
+    Xb = dev_t(d["X"], synth.F16)
+    X = Xb.repeat((M + base_rows - 1) // base_rows, 1)[:M].contiguous()
+    W, g, bias = dev_t(d["W"], synth.F16), dev_t(d["gamma"], synth.F16), dev_t(b, synth.F16)
+    rows = np.unique(np.concatenate([sample_rows(M, 12, seed=3), np.arange(M - 8, M)]))
+    x = w64(d, synth.F16)
+    xr = x["X"][rows % base_rows]
+    Y = lf.gemm_epilogue(X, W, bias, None, "gelu_tanh", out_dtype=T.float32)
+    got = to64(Y[T.as_tensor(rows, device="cuda:0")])
+    assert_close(got, oracle.gemm_epilogue(xr, x["W"], synth.widen(b, synth.F16), None, "gelu_tanh"), "gelu rows")
+    del Y
+    Y = lf.rmsnorm_gemm(X, g, W, EPS, out_dtype=T.float32)
+    got = to64(Y[T.as_tensor(rows, device="cuda:0")])
+    assert_close(got, oracle.rmsnorm_gemm(xr, x["gamma"], EPS32, x["W"]), "rms rows")
+    del Y, X
