@@ -61,7 +61,7 @@ constexpr Plan kPlans[] = {
     {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, 2, 2, 1, false, true},
     {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, 2, 2, 1, false, false},
     {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, 2, 2, 1, false, false},
-    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 2, 2, 1, true, false},
+    {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 4, 1, 1, true, false},
     {"reg_dual_256x128x64", Kind::Reg, 256, 128, 64, 2, 2, 2, 1, true, false},
     {"dma_256x256x32_s4_w8", Kind::Dma, 256, 256, 32, 4, 2, 4, 1, false, false},
     {"dma_128x128x64_s4_g2", Kind::Dma, 128, 128, 64, 4, 2, 2, 2, false, true},
