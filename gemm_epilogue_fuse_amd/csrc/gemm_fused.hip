@@ -57,7 +57,7 @@ struct Plan {
 };
 
 constexpr Plan kPlans[] = {
-    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, 2, 2, 1, false, false},
+    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, 2, 2, 1, false, false},  // RMS calls: 4 x 1 waves
     {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, 2, 2, 1, false, true},
     {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, 2, 2, 1, false, false},
     {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, 2, 2, 1, false, false},

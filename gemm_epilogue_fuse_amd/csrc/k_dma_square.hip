@@ -13,6 +13,9 @@ const void* square(const KernelSel& s) {
     using namespace dev;
     switch (s.plan) {
     case kDma256:
+        // RMS: 4 x 1 waves, so every A row is scaled by gamma in one wave only
+        if constexpr (RMS)
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 4, 1, 1, false, BF, true, 1, false>);
         return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 2, 1, false, BF, RMS, 1, false>);
     case kDma256W8:
         return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, false, BF, RMS, 1, false>);
