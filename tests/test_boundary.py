@@ -179,6 +179,29 @@ def test_plans(L):
             lf.set_plan(bad)
 
 
+def test_forced_plan_applies_only_where_it_fits(L):
+    """A forced plan serves the calls it fits; the others keep the automatic
+    choice (the header's contract for fuse_set_plan)."""
+    auto_single = lf.plan_name(1, 512, 4096, 4096)
+    auto_dual = lf.plan_name(2, 2048, 11008, 4096, lf.BF16)
+    lf.set_plan("dma_dual_256x128x32_s4")          # a gate/up plan: not used by the single-GEMM ops
+    try:
+        assert lf.plan_name(1, 512, 4096, 4096) == auto_single
+        assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == "dma_dual_256x128x32_s4"
+    finally:
+        lf.set_plan(None)
+    lf.set_plan("wstrip_16x16")                    # needs K % 256 == 0 and K <= 4096
+    try:
+        assert lf.plan_name(1, 8, 1024, 1024) == "wstrip_16x16"
+        assert lf.plan_name(1, 8, 1024, 8192) != "wstrip_16x16"
+        assert lf.plan_name(1, 8, 1024, 1000) != "wstrip_16x16"
+        assert lf.plan_name(2, 2048, 11008, 4096, lf.BF16) == auto_dual
+    finally:
+        lf.set_plan(None)
+    lf.set_plan("")                                 # "" restores the automatic choice too
+    assert lf.plan_name(1, 512, 4096, 4096) == auto_single
+
+
 def test_python_binding_rejects_bad_tensors():
     import torch
     # host tensors are refused outright: there is no CPU path
