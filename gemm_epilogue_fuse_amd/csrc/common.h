@@ -146,6 +146,174 @@ __device__ __forceinline__ float apply_act(float z) {
     else return z;
 }
 
+// ---------------------------------------------------------------- RMS range check and exact path
+//
+// The fast RMS path multiplies each X element by gamma on its way to the matrix
+// cores, rounds that product to the input type, and applies the row factor
+// r = 1/sqrt(mean(x^2) + eps) to the fp32 accumulator; the sum of squares is
+// accumulated in fp32.  x * r * gamma = r * (x * gamma) exactly, but the two
+// roundings differ in range: round(x * gamma) overflows the fp16 maximum when
+// |x * gamma| >= 65520 even though x * r * gamma is small; for a row whose mean
+// square plus eps is tiny, r multiplies the absolute rounding error of subnormal
+// products; and in bf16 the fp32 sum of squares can overflow.  A workgroup
+// therefore checks its rows after the reduction -- mean square plus eps inside
+// [lo, hi] and every accumulator finite (an operand that overflowed leaves an
+// inf or NaN in every column of its row) -- and if any row fails, recomputes
+// its whole tile with rms_exact_tile: r in fp64, the normalised activation
+// x * r * gamma (deplodock post, RMSNorm loop nest; "LLMBoost", section 3) as
+// an fp32 operand, products accumulated in fp32.  Inside the window the fast
+// path's operand error stays at or below the rounding of the normalised value
+// itself: an fp16 subnormal product is off by at most 2^-25, times r <= 2^15.
+
+constexpr float kRmsLoF16 = 0x1p-30f;    // mean square + eps below this: fp16 subnormal rounding matters
+constexpr float kRmsLoBF16 = 0x1p-120f;  // bf16 (and fp32) subnormal range
+constexpr float kRmsHi = 0x1p100f;       // mean square above this: the fp32 sum of squares nears overflow
+
+template <bool BF>
+__device__ __forceinline__ bool rms_outside(float ss, int K, float eps) {
+    const float ms = ss / (float)K;
+    return !(ms + eps >= (BF ? kRmsLoBF16 : kRmsLoF16)) || !(ms <= kRmsHi);
+}
+
+// Recompute output rows [m0, m0 + BM) x columns [n0, n0 + BN) of an RMS call
+// (NB = 2: the SwiGLU gate/up pair, H = SiLU(g) * u) from global memory with
+// plain arithmetic.  Every thread of the NT-thread workgroup calls it; `lds`
+// needs 16 * 8 + 16 * 64 * 4 bytes.  Slow (no matrix cores, no staging of W),
+// and only reached by tiles holding rows outside the fast path's window.
+template <bool BF, int NB, int NT, int BN>
+__device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0, int BM, int n0) {
+    constexpr int RC = 16, KC = 64, NW = NT / 64;
+    static_assert(NT % BN == 0, "whole threads per output column");
+    constexpr int TPC = NT / BN;               // threads per output column
+    static_assert(TPC >= RC || RC % TPC == 0, "rows of a chunk split evenly");
+    constexpr int RPT = (RC + TPC - 1) / TPC;  // rows of a chunk per thread
+    double* rr = reinterpret_cast<double*>(lds);
+    float* op = reinterpret_cast<float*>(lds + RC * sizeof(double));
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int N = p.N, K = p.K;
+    const int rows = min(BM, p.M - m0);
+    const int c = tid % BN, rsub = tid / BN;
+    const bool mine = n0 + c < N && rsub < RC;
+    __syncthreads();  // the caller's LDS use is over
+    for (int r0 = 0; r0 < rows; r0 += RC) {
+        const int rc = min(RC, rows - r0);
+        // r = 1 / sqrt(mean_k x^2 + eps) in fp64, one wave per row
+        for (int i = wave; i < rc; i += NW) {
+            const uint16_t* x = p.A + (size_t)(m0 + r0 + i) * K;
+            double s = 0.0;
+            for (int k = lane; k < K; k += 64) {
+                const double v = (double)h_f32<BF>(x[k]);
+                s = fma(v, v, s);
+            }
+            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+            if (lane == 0) rr[i] = 1.0 / sqrt(s / (double)K + (double)p.eps);
+        }
+        float acc[NB][RPT];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) acc[b][j] = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += KC) {
+            __syncthreads();  // the row factors are written; the previous chunk is consumed
+            for (int e = tid; e < RC * KC; e += NT) {
+                const int i = e / KC, k = k0 + e % KC;
+                float v = 0.0f;
+                if (i < rc && k < K)
+                    v = (float)((double)h_f32<BF>(p.A[(size_t)(m0 + r0 + i) * K + k]) * rr[i] *
+                                (double)h_f32<BF>(p.gamma[k]));
+                op[e] = v;
+            }
+            __syncthreads();
+            if (mine) {
+                const int kn = min(KC, K - k0);
+                for (int kk = 0; kk < kn; ++kk) {
+                    const size_t wo = (size_t)(k0 + kk) * N + n0 + c;
+                    const float w0 = h_f32<BF>(p.W[wo]);
+                    const float w1 = (NB == 2) ? h_f32<BF>(p.W2[wo]) : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < RPT; ++j) {
+                        const float a = op[(rsub + j * TPC) * KC + kk];  // rows past rc hold zeros
+                        acc[0][j] = fmaf(a, w0, acc[0][j]);
+                        if constexpr (NB == 2) acc[NB - 1][j] = fmaf(a, w1, acc[NB - 1][j]);
+                    }
+                }
+            }
+        }
+        if (mine) {
+            const float bias = (NB == 1 && p.bias != nullptr) ? h_f32<BF>(p.bias[n0 + c]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < RPT; ++j) {
+                const int i = rsub + j * TPC;
+                if (i >= rc) continue;
+                float z;
+                if constexpr (NB == 2) {
+                    z = silu(acc[0][j]) * acc[NB - 1][j];
+                } else {
+                    z = acc[0][j] + bias;
+                    switch (p.act) {
+                    case 1: z = apply_act<1>(z); break;
+                    case 2: z = apply_act<2>(z); break;
+                    case 3: z = apply_act<3>(z); break;
+                    default: break;
+                    }
+                }
+                const size_t o = (size_t)(m0 + r0 + i) * N + n0 + c;
+                if (p.out_f32) static_cast<float*>(p.Y)[o] = z;
+                else static_cast<uint16_t*>(p.Y)[o] = f32_h<BF>(z);
+            }
+        }
+        __syncthreads();  // before the next chunk's row factors overwrite rr
+    }
+}
+
+// Finish and store 8 consecutive output columns [gcol, gcol + 8) of row grow:
+// r[m] (rsc), bias, activation, residual, one rounding, 16-byte stores.  Used by
+// the few-row kernels, where one thread owns such a piece.
+template <bool BF>
+__device__ __forceinline__ void finish_store8(const KArgs& p, float (&v)[8], float rsc, int grow, int gcol) {
+    const int N = p.N;
+    float bias8[8];
+    {
+        u32x4 bw = {0u, 0u, 0u, 0u};
+        if (p.bias != nullptr) bw = *reinterpret_cast<const u32x4*>(p.bias + gcol);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bias8[2 * q] = lo_f32<BF>(bw[q]);
+            bias8[2 * q + 1] = hi_f32<BF>(bw[q]);
+        }
+    }
+    u32x4 rw = {0u, 0u, 0u, 0u};
+    const bool has_res = p.resid != nullptr;
+    if (has_res) rw = *reinterpret_cast<const u32x4*>(p.resid + (size_t)grow * N + gcol);
+    auto finish = [&](auto ACT) {
+        constexpr int A = decltype(ACT)::value;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float z = v[e] * rsc + bias8[e];
+            z = apply_act<A>(z);
+            if (has_res) z += (e & 1) ? hi_f32<BF>(rw[e >> 1]) : lo_f32<BF>(rw[e >> 1]);
+            v[e] = z;
+        }
+    };
+    switch (p.act) {
+    case 1: finish(std::integral_constant<int, 1>{}); break;
+    case 2: finish(std::integral_constant<int, 2>{}); break;
+    case 3: finish(std::integral_constant<int, 3>{}); break;
+    default: finish(std::integral_constant<int, 0>{}); break;
+    }
+    const size_t o = (size_t)grow * N + gcol;
+    if (p.out_f32) {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.Y) + o);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        u32x4 ow;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ow[q] = pack2<BF>(v[2 * q], v[2 * q + 1]);
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.Y) + o) = ow;
+    }
+}
+
 // ---------------------------------------------------------------- schedule
 
 // Workgroups are handed to the 8 XCDs round-robin by id.  Give every XCD a

@@ -244,49 +244,24 @@ gemm_decode_kernel(const KArgs p) {
 
     // ---- epilogue: r[m], bias, activation, residual, one rounding, 16-byte store
     const int gcol = n0 + c0;
-    if (!row_ok || gcol >= N) return;  // N % 8 == 0: a thread's 8 columns are all in or all out
-    const int grow = m0 + row;
-    const float rsc = RMS ? 1.0f / sqrtf(srow / (float)K + p.eps) : 1.0f;
-    float bias8[8];
-    {
-        u32x4 bw = {0u, 0u, 0u, 0u};
-        if (p.bias != nullptr) bw = *reinterpret_cast<const u32x4*>(p.bias + gcol);
+    const bool active = row_ok && gcol < N;  // N % 8 == 0: a thread's 8 columns are all in or all out
+    if constexpr (RMS) {
+        // rows outside the fast path's range: recompute the tile exactly (an
+        // overflowed operand leaves non-finite sums)
+        bool bad = false;
+        if (active) {
+            float t = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bias8[2 * q] = lo_f32<BF>(bw[q]);
-            bias8[2 * q + 1] = hi_f32<BF>(bw[q]);
+            for (int e = 0; e < 8; ++e) t += v[e];
+            bad = rms_outside<BF>(srow, K, p.eps) || !__builtin_isfinite(t);
+        }
+        if (__syncthreads_or(bad)) {
+            rms_exact_tile<BF, 1, NT, BN>(p, smem, m0, BM, n0);
+            return;
         }
     }
-    u32x4 rw = {0u, 0u, 0u, 0u};
-    const bool has_res = p.resid != nullptr;
-    if (has_res) rw = *reinterpret_cast<const u32x4*>(p.resid + (size_t)grow * N + gcol);
-    auto finish = [&](auto ACT) {
-        constexpr int A = decltype(ACT)::value;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float z = (RMS ? v[e] * rsc : v[e]) + bias8[e];
-            z = apply_act<A>(z);
-            if (has_res) z += (e & 1) ? hi_f32<BF>(rw[e >> 1]) : lo_f32<BF>(rw[e >> 1]);
-            v[e] = z;
-        }
-    };
-    switch (p.act) {
-    case 1: finish(ic<1>{}); break;
-    case 2: finish(ic<2>{}); break;
-    case 3: finish(ic<3>{}); break;
-    default: finish(ic<0>{}); break;
-    }
-    const size_t o = (size_t)grow * N + gcol;
-    if (p.out_f32) {
-        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.Y) + o);
-        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
-        u32x4 ow;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ow[q] = pack2<BF>(v[2 * q], v[2 * q + 1]);
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.Y) + o) = ow;
-    }
+    if (!active) return;
+    finish_store8<BF>(p, v, RMS ? 1.0f / sqrtf(srow / (float)K + p.eps) : 1.0f, m0 + row, gcol);
 }
 
 }  // namespace dev

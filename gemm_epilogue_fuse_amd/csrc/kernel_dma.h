@@ -733,12 +733,31 @@ gemm_dma_kernel(const KArgs p) {
     float* rs = reinterpret_cast<float*>(smem + SMEM_MAIN);
     if constexpr (RMS) {
         // lanes l and l+32 hold the two k-halves of row l%32 of each block
+        bool bad = false;
 #pragma unroll
         for (int i = 0; i < FMO; ++i) {
             const float s = sso[i] + __shfl_xor(sso[i], 32);
-            if (wn == 0 && lane < 32) rs[wme * TME + i * 32 + lane] = 1.0f / sqrtf(s / (float)K + p.eps);
+            const int rl = wme * TME + i * 32 + (lane & 31);
+            if (wn == 0 && lane < 32) rs[rl] = 1.0f / sqrtf(s / (float)K + p.eps);
+            bad |= m0 + rl < M && rms_outside<BF>(s, K, p.eps);
         }
+        // an operand that overflowed leaves a non-finite accumulator (and
+        // the sum of non-finite and finite values is never finite)
+        float t = 0.0f;
+#pragma unroll
+        for (int o = 0; o < NB; ++o)
+#pragma unroll
+            for (int i = 0; i < FMO; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) t += acco[o][i][j][r];
+        bad |= !__builtin_isfinite(t);
         __syncthreads();
+        if (__syncthreads_or(bad)) {
+            rms_exact_tile<BF, NB, NT, BN>(p, smem, m0, BM, n0);
+            return;
+        }
     }
     Store::run(p, acco, reinterpret_cast<float*>(smem), rs, m0, n0, wme, wn);
 }

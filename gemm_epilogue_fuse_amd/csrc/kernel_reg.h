@@ -255,15 +255,34 @@ gemm_fused_kernel(const KArgs p) {
     // loaded the same row, then r = 1/sqrt(ss/K + eps) into LDS.
     float* rs = reinterpret_cast<float*>(lds + 2 * STAGE);
     if constexpr (RMS) {
+        bool bad = false;
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             float s = ss[i];
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
             s += __shfl_xor(s, 4);
-            if (a_kc == 0) rs[a_row0 + i * A_ROW_STEP] = 1.0f / sqrtf(s / (float)K + p.eps);
+            const int row = a_row0 + i * A_ROW_STEP;
+            if (a_kc == 0) rs[row] = 1.0f / sqrtf(s / (float)K + p.eps);
+            bad |= m0 + row < M && rms_outside<BF>(s, K, p.eps);
         }
+        // rows outside the fast path's range: recompute the tile exactly
+        // (an overflowed operand leaves a non-finite accumulator)
+        float t = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) t += acc[b][i][j][r];
+        bad |= !__builtin_isfinite(t);
         __syncthreads();
+        if (__syncthreads_or(bad)) {
+            rms_exact_tile<BF, NB, NT, BN>(p, reinterpret_cast<char*>(lds), m0, BM, n0);
+            return;
+        }
     }
 
     using Store = TileStore<BM, BN, WM, WN, BF, RMS, NB>;

@@ -3,8 +3,8 @@ MI355X).
 
 Small and ragged shapes are compared element by element over the whole
 output, with every tile plan forced in turn; the workloads at their full
-sizes run in the automatic plan (the one the bench times) and are compared on
-sampled rows, which the oracle computes exactly because rows are independent.
+sizes run in the automatic plan (the one the bench times) and are compared
+with the oracle over their whole output, written into NaN-filled buffers.
 Tolerance: max_abs_err <= 1.5e-2 and mean_abs_err <= 1.5e-3.  bf16 runs are
 checked with a float32 output against that bound (a bf16 output alone can be
 off by half a bf16 ulp, 0.0156 at |y| in [4, 8), for any implementation), and
@@ -17,41 +17,10 @@ import pytest
 import gemm_epilogue_fuse_amd as lf
 import oracle
 import synth
-from parity_util import EPS, EPS32, assert_close, dev_t, sample_rows, say, to64
+from parity_util import DUAL_PLANS, EPS, EPS32, PLANS, assert_close, dev_t, fitk, say, to64
 
 pytestmark = pytest.mark.gpu
 
-# Tile plans, and DMA plans with a forced split-K count (":k<S>"): the
-# splits of a tile are reduced in a fixed order by the last one to finish.
-PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64",
-         "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
-         "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
-         "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
-         "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
-         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2", "wstrip_16x16", "wstrip_32x16",
-         "dma_64x128x64_s4_g2", "dma_64x128x64_s4_g2:k3"]
-# Gate/up dual-GEMM plans ("" = automatic choice); a forced DMA plan applies where K
-# is a multiple of its K step, the automatic choice elsewhere.
-DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]
-
-
-def fitk(plan, K):
-    """DMA and small-M plans need K % 64 == 0 (strips K % 128, whole strips K % 256): round K up for them
-    (M and N stay ragged);
-    split plans get at least 3 K steps per split."""
-    if not plan.startswith(("dma", "dec", "strip", "wstrip")):
-        return K
-    step = 256 if plan.startswith("wstrip") else 128 if plan.startswith("strip") else 64
-    K = -(-K // step) * step
-    if plan.startswith("dec") and ":k" not in plan:
-        K = min(K, 512)  # one K chunk: at most 8 steps of 64
-    if ":k" in plan:
-        K = max(K, 64 * 3 * int(plan.split(":k")[1]))
-    return K
-
-
-def base(plan):
-    return plan.split(":")[0]
 ACTS = ["none", "relu", "gelu_tanh", "silu"]
 
 
@@ -159,17 +128,6 @@ def test_swiglu_ragged(dual_plan, dtype, M, F, K):
         check_bf16_output(out16, out32, want, "H")
 
 
-def test_small_workload_gemm_bias_gelu():
-    """64x256x256 GEMM + bias + GeLU, fp16, seed 0: the whole output."""
-    say("C1 64x256x256 gelu fp16")
-    d = synth.gemm_bias_gelu_small(seed=0)
-    t = {k: dev_t(v, synth.F16) for k, v in d.items()}
-    x = w64(d, synth.F16)
-    want = oracle.gemm_epilogue(x["A"], x["W"], x["bias"], None, "gelu_tanh")
-    got = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], None, "gelu_tanh"))
-    assert_close(got, want, "C1")
-
-
 @pytest.mark.parametrize("wplan", ["wstrip_16x16", "wstrip_32x16"])
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 @pytest.mark.parametrize("M,N,K", [(1, 264, 1280), (5, 136, 2048), (17, 520, 3072), (32, 4104, 4096)])
@@ -200,45 +158,75 @@ def test_whole_strip_long_k(wplan, dtype, M, N, K):
 
 
 # --------------------------------------------------------------------------- full sizes (automatic plan)
+#
+# Every workload at its full size, in the plan the bench times, compared with
+# the oracle over the whole output.  Outputs are pre-filled with NaN, so an
+# element no workgroup writes (a skipped tile, a dropped tail) fails the
+# finiteness check, and one written twice with different values fails the
+# comparison.
+
+def nan_out(shape, dtype):
+    T = torch()
+    return T.full(shape, float("nan"), dtype=dtype, device="cuda:0")
+
+
+def test_small_workload_gemm_bias_gelu():
+    """64x256x256 GEMM + bias + GeLU, fp16, seed 0: the whole output."""
+    T = torch()
+    say("C1 64x256x256 gelu fp16", lf.plan_name(0, 64, 256, 256))
+    d = synth.gemm_bias_gelu_small(seed=0)
+    t = {k: dev_t(v, synth.F16) for k, v in d.items()}
+    x = w64(d, synth.F16)
+    want = oracle.gemm_epilogue(x["A"], x["W"], x["bias"], None, "gelu_tanh")
+    got = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], None, "gelu_tanh", out=nan_out((64, 256), T.float16)))
+    assert_close(got, want, "C1")
+
 
 def test_prefill_rmsnorm_linear_512x4096x4096():
+    T = torch()
     say("C2 rmsnorm->linear 512x4096x4096 fp16", lf.plan_name(1, 512, 4096, 4096))
     d = synth.rmsnorm_linear(M=512, D=4096, N=4096, seed=0)
     t = {k: dev_t(v, synth.F16) for k, v in d.items()}
     x = w64(d, synth.F16)
-    Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS))
-    rows = sample_rows(512, 32)
-    want = oracle.rmsnorm_gemm(x["X"][rows], x["gamma"], EPS32, x["W"])
-    assert_close(Y[rows], want, "C2 rows")
-    assert np.all(np.isfinite(Y))
+    Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, out=nan_out((512, 4096), T.float16)))
+    want = oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["W"])
+    assert_close(Y, want, "C2 whole output")
 
 
 @pytest.mark.parametrize("M", [512, 1024, 2048, 4096])
 def test_gemm_bias_gelu_sweep(M):
+    T = torch()
     say("C3 gelu sweep M=%d" % M, lf.plan_name(0, M, 4096, 4096))
     d = synth.gemm_epilogue_sweep(M, seed=0)
     t = {k: dev_t(v, synth.F16) for k, v in d.items()}
-    Y = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], None, "gelu_tanh"))
-    rows = sample_rows(M, 16)
+    Y = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], None, "gelu_tanh", out=nan_out((M, 4096), T.float16)))
     x = w64(d, synth.F16)
-    want = oracle.gemm_epilogue(x["A"][rows], x["W"], x["bias"], None, "gelu_tanh")
-    assert_close(Y[rows], want, "C3 M=%d" % M)
-    assert np.all(np.isfinite(Y))
+    want = oracle.gemm_epilogue(x["A"], x["W"], x["bias"], None, "gelu_tanh")
+    assert_close(Y, want, "C3 M=%d whole output" % M)
 
 
 @pytest.mark.parametrize("variant", ["silu", "relu", "residual"])
 def test_gemm_epilogue_variants_4096(variant):
+    T = torch()
     M = 4096
-    say("C3 variant", variant)
+    say("C3 variant", variant, lf.plan_name(0, M, 4096, 4096))
     d = synth.gemm_epilogue_sweep(M, seed=0, residual=(variant == "residual"))
     t = {k: dev_t(v, synth.F16) for k, v in d.items()}
     x = w64(d, synth.F16)
     act = "none" if variant == "residual" else variant
     R = t.get("R")
-    Y = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], R, act))
-    rows = sample_rows(M, 16)
-    want = oracle.gemm_epilogue(x["A"][rows], x["W"], x["bias"], x["R"][rows] if R is not None else None, act)
-    assert_close(Y[rows], want, "C3 %s" % variant)
+    Y = to64(lf.gemm_epilogue(t["A"], t["W"], t["bias"], R, act, out=nan_out((M, 4096), T.float16)))
+    want = oracle.gemm_epilogue(x["A"], x["W"], x["bias"], x["R"] if R is not None else None, act)
+    assert_close(Y, want, "C3 %s whole output" % variant)
+
+
+def swiglu_sensitivity(x):
+    """|dH/dg| + |dH/du| for H = SiLU(g) u, at the oracle's gate and up projections
+    g = RMSNorm(X) Wg and u = RMSNorm(X) Wu."""
+    g = oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["Wg"])
+    u = oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["Wu"])
+    sig = 1.0 / (1.0 + np.exp(-g))
+    return np.abs(u * sig * (1.0 + g * (1.0 - sig))) + np.abs(g * sig)
 
 
 def test_swiglu_ffn_bf16_full():
@@ -248,28 +236,32 @@ def test_swiglu_ffn_bf16_full():
     d = synth.swiglu_ffn(M=M, D=D, F=F, seed=0)
     t = {k: dev_t(v, synth.BF16) for k, v in d.items()}
     x = w64(d, synth.BF16)
-    rows = sample_rows(M, 12)
     # kernel 1: H = SiLU(Xhat Wg) * (Xhat Wu)
-    H16 = lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], EPS)
-    H32 = to64(lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], EPS, out_dtype=T.float32))
-    Hw = oracle.rmsnorm_swiglu(x["X"][rows], x["gamma"], EPS32, x["Wg"], x["Wu"])
-    # H = SiLU(g) * u multiplies two unit-scale projections and reaches |H| ~ 20;
-    # the bf16 rounding of the normalised operand gives it an error that grows
-    # with |H|, so the intermediate is compared after scaling by max(1, |H|).
+    H16 = lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], EPS, out=nan_out((M, F), T.bfloat16))
+    H32 = to64(lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], EPS, out_dtype=T.float32,
+                                      out=nan_out((M, F), T.float32)))
+    Hw = oracle.rmsnorm_swiglu(x["X"], x["gamma"], EPS32, x["Wg"], x["Wu"])
+    # H = SiLU(g) * u is a nonlinear function of the two projections g and u,
+    # which carry the tolerance: the bf16 rounding of the normalised operand
+    # (which any bf16 matrix-core path has) perturbs g and u by about 1e-3,
+    # and H moves by |dH/dg| |dg| + |dH/du| |du|.  So H's error is compared
+    # after dividing by max(1, |dH/dg| + |dH/du|) at the oracle's g and u.
     # The block output Y below is held to the plain absolute tolerance.
-    scale = np.maximum(1.0, np.abs(Hw))
-    assert_close(H32[rows] / scale, Hw / scale, "C4 k1 f32out (scaled by max(1,|H|))")
-    check_bf16_output(to64(H16)[rows], H32[rows], Hw, "C4 k1")
-    # kernel 2 on the H the GPU produced: Y = H Wd + b + X
-    Y32 = to64(lf.gemm_epilogue(H16, t["Wd"], t["bias"], t["X"], "none", out_dtype=T.float32))
+    scale = np.maximum(1.0, swiglu_sensitivity(x))
+    assert_close(H32 / scale, Hw / scale, "C4 k1 f32out (relative to H's sensitivity to g and u)")
     Hg = to64(H16)
-    want2 = oracle.gemm_epilogue(Hg[rows], x["Wd"], x["bias"], x["X"][rows], "none")
-    assert_close(Y32[rows], want2, "C4 k2 f32out")
-    # whole block against the oracle's unrounded FFN
-    want = oracle.swiglu_ffn(x["X"][rows], x["gamma"], EPS32, x["Wg"], x["Wu"], x["Wd"], x["bias"])
-    assert_close(Y32[rows], want, "C4 block f32out")
-    Y16 = to64(lf.gemm_epilogue(H16, t["Wd"], t["bias"], t["X"], "none"))
-    check_bf16_output(Y16[rows], Y32[rows], want, "C4 block")
+    check_bf16_output(Hg, H32, Hw, "C4 k1")
+    # kernel 2 on the H the GPU produced: Y = H Wd + b + X
+    Y32 = to64(lf.gemm_epilogue(H16, t["Wd"], t["bias"], t["X"], "none", out_dtype=T.float32,
+                                out=nan_out((M, D), T.float32)))
+    want2 = oracle.gemm_epilogue(Hg, x["Wd"], x["bias"], x["X"], "none")
+    assert_close(Y32, want2, "C4 k2 f32out")
+    # whole block against the oracle's unrounded FFN: the oracle's down
+    # projection applied to the oracle's H (the composition swiglu_ffn defines)
+    want = oracle.gemm_epilogue(Hw, x["Wd"], x["bias"], x["X"], "none")
+    assert_close(Y32, want, "C4 block f32out")
+    Y16 = to64(lf.gemm_epilogue(H16, t["Wd"], t["bias"], t["X"], "none", out=nan_out((M, D), T.bfloat16)))
+    check_bf16_output(Y16, Y32, want, "C4 block")
 
 
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
@@ -281,24 +273,25 @@ def test_decode_rmsnorm_linear_sweep(B, D, dtype):
     d = synth.decode_rmsnorm_linear(B, D, seed=0, dtype=dtype)
     t = {k: dev_t(v, dtype) for k, v in d.items()}
     x = w64(d, dtype)
-    rows = sample_rows(B, 16)
-    want = oracle.rmsnorm_gemm(x["X"][rows], x["gamma"], EPS32, x["W"])
+    want = oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["W"])
     if dtype == synth.F16:
-        Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS))
-        assert_close(Y[rows], want, "C5 f16")
+        Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, out=nan_out((B, D), T.float16)))
+        assert_close(Y, want, "C5 f16 whole output")
     else:
-        Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, out_dtype=T.float32))
-        assert_close(Y[rows], want, "C5 bf16 f32out")
-        Y16 = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS))
-        check_bf16_output(Y16[rows], Y[rows], want, "C5")
+        Y = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, out_dtype=T.float32,
+                                 out=nan_out((B, D), T.float32)))
+        assert_close(Y, want, "C5 bf16 f32out whole output")
+        Y16 = to64(lf.rmsnorm_gemm(t["X"], t["gamma"], t["W"], EPS, out=nan_out((B, D), T.bfloat16)))
+        check_bf16_output(Y16, Y, want, "C5")
 
 
-def test_largest_accepted_shape_sampled_rows():
+def test_largest_accepted_shape_whole_output():
     """M = 131064, K = N = 4096: M*K is just under the 2^29-element limit of the
     ABI (A and Y are 1 GiB each in fp16) and the last 256-row tile is ragged.
-    A repeats a seeded 4096-row block, so each sampled row has an oracle value;
-    rows from the first, middle and last tiles are checked, for the GEMM +
-    bias + GeLU and for RMSNorm -> Linear."""
+    A repeats a seeded 4096-row block, so the oracle's output for that block
+    is the expected value of every row; all 131064 rows are compared (on the
+    device, block by block), for the GEMM + bias + GeLU and for RMSNorm ->
+    Linear."""
     T = torch()
     M, K, N, base_rows = 131064, 4096, 4096, 4096
     assert M * K < (1 << 29) and (M + 8) * K >= (1 << 29)
@@ -308,14 +301,24 @@ def test_largest_accepted_shape_sampled_rows():
     Xb = dev_t(d["X"], synth.F16)
     X = Xb.repeat((M + base_rows - 1) // base_rows, 1)[:M].contiguous()
     W, g, bias = dev_t(d["W"], synth.F16), dev_t(d["gamma"], synth.F16), dev_t(b, synth.F16)
-    rows = np.unique(np.concatenate([sample_rows(M, 12, seed=3), np.arange(M - 8, M)]))
     x = w64(d, synth.F16)
-    xr = x["X"][rows % base_rows]
-    Y = lf.gemm_epilogue(X, W, bias, None, "gelu_tanh", out_dtype=T.float32)
-    got = to64(Y[T.as_tensor(rows, device="cuda:0")])
-    assert_close(got, oracle.gemm_epilogue(xr, x["W"], synth.widen(b, synth.F16), None, "gelu_tanh"), "gelu rows")
+
+    def compare(Y, want64, what):
+        want = T.from_numpy(want64).to("cuda:0")
+        mx, tot = 0.0, 0.0
+        for r0 in range(0, M, base_rows):
+            blk = Y[r0:r0 + base_rows]
+            diff = (blk.double() - want[:blk.shape[0]]).abs()
+            assert bool(T.isfinite(blk).all()), "%s: non-finite output in rows %d.." % (what, r0)
+            mx = max(mx, float(diff.max()))
+            tot += float(diff.sum())
+        mean = tot / (M * N)
+        say("  %s max_abs_err=%.3e mean_abs_err=%.3e" % (what, mx, mean))
+        assert mx <= 1.5e-2 and mean <= 1.5e-3, (what, mx, mean)
+
+    Y = lf.gemm_epilogue(X, W, bias, None, "gelu_tanh", out_dtype=T.float32, out=nan_out((M, N), T.float32))
+    compare(Y, oracle.gemm_epilogue(x["X"], x["W"], synth.widen(b, synth.F16), None, "gelu_tanh"), "gelu all rows")
     del Y
-    Y = lf.rmsnorm_gemm(X, g, W, EPS, out_dtype=T.float32)
-    got = to64(Y[T.as_tensor(rows, device="cuda:0")])
-    assert_close(got, oracle.rmsnorm_gemm(xr, x["gamma"], EPS32, x["W"]), "rms rows")
+    Y = lf.rmsnorm_gemm(X, g, W, EPS, out_dtype=T.float32, out=nan_out((M, N), T.float32))
+    compare(Y, oracle.rmsnorm_gemm(x["X"], x["gamma"], EPS32, x["W"]), "rms all rows")
     del Y, X

@@ -13,39 +13,10 @@ import pytest
 import gemm_epilogue_fuse_amd as lf
 import oracle
 import synth
-from parity_util import dev_t, say, to64
+from parity_util import DUAL_PLANS, PLANS, base, dev_t, fitk, say, to64
 
 pytestmark = pytest.mark.gpu
 
-# Tile plans, and DMA plans with a forced split-K count (":k<S>"): the
-# splits of a tile are reduced in a fixed order by the last one to finish.
-PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x128x64",
-         "dma_128x128x64_s4:k3", "dma_128x128x64_s4:k2", "dma_256x256x32_s4_w8",
-         "dma_128x128x64_s4_g2", "dma_128x128x64_s4_g2:k2", "dma_128x128x64_s4_g2:k3",
-         "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
-         "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
-         "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2", "wstrip_16x16", "wstrip_32x16",
-         "dma_64x128x64_s4_g2", "dma_64x128x64_s4_g2:k3"]
-DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]
-
-
-def fitk(plan, K):
-    """DMA and small-M plans need K % 64 == 0 (strips K % 128, whole strips K % 256): round K up for them
-    (M and N stay ragged);
-    split plans get at least 3 K steps per split."""
-    if not plan.startswith(("dma", "dec", "strip", "wstrip")):
-        return K
-    step = 256 if plan.startswith("wstrip") else 128 if plan.startswith("strip") else 64
-    K = -(-K // step) * step
-    if plan.startswith("dec") and ":k" not in plan:
-        K = min(K, 512)  # one K chunk: at most 8 steps of 64
-    if ":k" in plan:
-        K = max(K, 64 * 3 * int(plan.split(":k")[1]))
-    return K
-
-
-def base(plan):
-    return plan.split(":")[0]
 DTYPES = [synth.F16, synth.BF16]
 ONE = {synth.F16: 0x3C00, synth.BF16: 0x3F80}
 SHAPES = [(1, 8, 8), (7, 24, 40), (65, 136, 72), (129, 264, 200), (300, 392, 328), (520, 776, 264)]
@@ -317,3 +288,51 @@ def test_graph_replay_matches_eager(plan_name):
                 assert torch.equal(o.view(torch.int32), ref.view(torch.int32))
     finally:
         lf.set_plan(None)
+
+
+# --------------------------------------------------------------------------- full sizes, automatic plans
+#
+# The multi-group tile order, uneven XCD remainders, split-K counts above 3
+# and the decode kernel's long chunk lists only occur at full size.  Small
+# integer data keeps every fp32 partial sum exact in any order, so the whole
+# output must equal the oracle bit for bit (float32 output: the sums reach
+# several thousand).
+
+FULL_SHAPES = [(4096, 4096, 4096), (512, 4096, 4096), (2048, 4096, 11008), (2048, 11008, 4096),
+               (1024, 4096, 4096), (128, 4096, 4096), (32, 4096, 4096), (1, 4096, 4096), (130, 4104, 2048)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N,K", FULL_SHAPES)
+def test_integer_data_bit_exact_full_size(dtype, M, N, K):
+    import torch
+    say("integer full size", dtype, M, N, K, lf.plan_name(0, M, N, K, lf.BF16 if dtype == synth.BF16 else lf.F16))
+    g = synth.generator(M + 3 * N + 7 * K)
+    A = g.integers(-1, 2, (M, K)).astype(np.float64)
+    W = g.integers(-1, 2, (K, N)).astype(np.float64)
+    b = g.integers(-100, 101, N).astype(np.float64)
+    R = g.integers(-100, 101, (M, N)).astype(np.float64)
+    bits = {k: synth.to_bits(v, dtype) for k, v in (("A", A), ("W", W), ("b", b), ("R", R))}
+    t = {k: dev_t(v, dtype) for k, v in bits.items()}
+    want = oracle.gemm_epilogue(A, W, b, R, "relu")
+    Y = lf.gemm_epilogue(t["A"], t["W"], t["b"], t["R"], "relu", out_dtype=torch.float32,
+                         out=nan_filled((M, N), torch.float32))
+    got = to64(Y)
+    assert np.array_equal(got, want), np.nanmax(np.abs(got - want))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,K", [(512, 4096), (2048, 4096), (1, 4096), (32, 4096), (128, 2048), (1024, 1024)])
+def test_rmsnorm_exact_rows_full_size(dtype, M, K):
+    """eps = 0, rows of +-1 and +-2 (r = 1 and 1/2 exactly), W = I: the output
+    is sign * gamma bit for bit, through the automatic plan (split K, decode
+    chunks) at full size."""
+    say("rms-exact full size", dtype, M, K, lf.plan_name(1, M, K, K, lf.BF16 if dtype == synth.BF16 else lf.F16))
+    g = synth.generator(11 + M + K)
+    sign = g.choice([-1.0, 1.0], size=(M, K))
+    X = sign * np.where(np.arange(M) % 2 == 0, 1.0, 2.0)[:, None]
+    gamma = synth.widen(synth.to_bits(1.0 + 0.1 * g.standard_normal(K), dtype), dtype)
+    Xt = dev_t(synth.to_bits(X, dtype), dtype)
+    Y = lf.rmsnorm_gemm(Xt, dev_t(synth.to_bits(gamma, dtype), dtype), dev_t(eye_bits(K, K, dtype), dtype),
+                        eps=0.0, out=nan_filled((M, K), Xt.dtype))
+    assert np.array_equal(to64(Y), sign * gamma[None, :])
