@@ -16,6 +16,7 @@ import os
 
 __all__ = [
     "gemm_epilogue", "rmsnorm_gemm", "rmsnorm_gemm_swiglu", "swiglu_ffn", "plan_name", "set_plan",
+    "workspace_bytes",
     "FuseError", "lib", "LIB_PATH", "ACT", "F16", "BF16", "OUT_F32",
 ]
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.fuse_rmsnorm_gemm_swiglu.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, vp]
         L.fuse_plan_name.restype = ctypes.c_char_p
         L.fuse_plan_name.argtypes = [ci, i64, i64, i64, ci]
+        L.fuse_workspace_bytes.restype = i64
+        L.fuse_workspace_bytes.argtypes = [ci, i64, i64, i64, ci]
         L.fuse_set_plan.restype = ci
         L.fuse_set_plan.argtypes = [ctypes.c_char_p]
         L.fuse_strerror.restype = ctypes.c_char_p
@@ -197,6 +200,14 @@ def swiglu_ffn(X, gamma, Wg, Wu, Wd, bias_d, eps=1e-6, out_dtype=None, H=None, o
 
 def plan_name(op: int, M: int, N: int, K: int, dtype: int = F16) -> str:
     return lib().fuse_plan_name(op, M, N, K, dtype).decode()
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int, dtype: int = F16) -> int:
+    """Bytes of split-K workspace a call would use (0: its plan does not split K)."""
+    n = lib().fuse_workspace_bytes(op, M, N, K, dtype)
+    if n < 0:
+        raise ValueError("invalid op, dtype or shape")
+    return n
 
 
 def set_plan(name):

@@ -180,6 +180,20 @@ const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype) {
     return lf::plan_name(p);
 }
 
+int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype) {
+    if (op < 0 || op > 2) return -1;
+    bool bf16 = false, out_f32 = false;
+    if (check_dtype(dtype, &bf16, &out_f32) != FUSE_OK || check_dims(M, N, K) != FUSE_OK) return -1;
+    lf::Problem p{};
+    p.op = static_cast<lf::Op>(op);
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.bf16 = bf16;
+    p.out_f32 = out_f32;
+    return static_cast<int64_t>(lf::workspace_bytes(p));
+}
+
 int fuse_set_plan(const char* name) { return lf::set_plan(name) ? FUSE_OK : FUSE_E_ENUM; }
 
 const char* fuse_strerror(int status) {

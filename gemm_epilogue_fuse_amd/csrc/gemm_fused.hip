@@ -30,6 +30,8 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
+#include <algorithm>
 
 #include "common.h"
 #include "kernel_strip.h"
@@ -191,39 +193,60 @@ Choice choose(const Problem& p) {
 }
 
 // Split-K workspace, one per (device, stream) so calls on different
-// streams never share partials or counters.  Grown on demand; the counters
-// are zeroed once at allocation and every reducing workgroup puts its
-// counter back to zero.
+// streams never share partials or counters.  It grows geometrically on
+// demand; a buffer it outgrows is retired, never freed, because a HIP graph
+// captured earlier may still hold its address.  The arrival counters of a new
+// buffer are zeroed by a fill kernel on the caller's stream (stream-ordered
+// before the call that needs them); every reducing workgroup puts its counter
+// back to zero.  The lock is held from the lookup through the launch, so a
+// second host thread on the same stream cannot retire the buffer in between.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<void*> g_ws_retired;
 constexpr size_t kCounterBytes = 1 << 20;  // 256K tiles
+constexpr size_t kMinWorkspace = size_t(64) << 20;
 
+__global__ void __launch_bounds__(256) zero_words_kernel(unsigned* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t zero_words(unsigned* p, size_t bytes, hipStream_t stream) {
+    const int n = (int)(bytes / sizeof(unsigned));
+    void* args[] = {&p, const_cast<int*>(&n)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&zero_words_kernel), dim3((n + 255) / 256), dim3(256),
+                           args, 0, stream);
+}
+
+// Caller holds g_ws_mu.
 hipError_t get_workspace(hipStream_t stream, size_t part_bytes, float** ws, unsigned** cnt) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[{dev, stream}];
     const size_t need = kCounterBytes + part_bytes;
     if (w.bytes < need) {
-        if (w.ptr) {
-            // the old buffer may still be in use by queued work on this stream
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return e;
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
+        // allocating inside a stream capture is not allowed: capture after
+        // an eager call on this stream that needed at least as much
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return e;
+        if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+        const size_t bytes = std::max({need, kMinWorkspace, 2 * w.bytes});
+        void* ptr = nullptr;
+        e = hipMalloc(&ptr, bytes);
+        if (e != hipSuccess) return e;
+        e = zero_words(static_cast<unsigned*>(ptr), kCounterBytes, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(ptr);
+            return e;
         }
-        const size_t bytes = std::max(need, size_t(64) << 20);
-        e = hipMalloc(&w.ptr, bytes);
-        if (e != hipSuccess) return e;
-        e = hipMemset(w.ptr, 0, kCounterBytes);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e != hipSuccess) return e;
+        if (w.ptr) g_ws_retired.push_back(w.ptr);
+        w.ptr = ptr;
         w.bytes = bytes;
     }
     *cnt = static_cast<unsigned*>(w.ptr);
@@ -290,11 +313,12 @@ bool set_plan(const char* name) {
     return false;
 }
 
-hipError_t launch(const Problem& p, hipStream_t stream) {
-    if (p.M == 0) return hipSuccess;
+namespace {
+
+// Kernel arguments of a call (without the workspace pointers) and its plan.
+Choice setup(const Problem& p, KArgs& a) {
     const Choice c = choose(p);
     const Plan& pl = *c.plan;
-    KArgs a;
     a.A = static_cast<const uint16_t*>(p.A);
     a.W = static_cast<const uint16_t*>(p.W);
     a.W2 = static_cast<const uint16_t*>(p.W2);
@@ -307,7 +331,8 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     a.K = (int)p.K;
     a.tiles_m = (int)((p.M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((p.N + pl.bn - 1) / pl.bn);
-    a.group_m = (pl.kind == Kind::Dec || pl.kind == Kind::Strip || pl.kind == Kind::WStrip) ? a.tiles_m : 4;  // small M: the row tiles of a W column tile share an XCD
+    // small M: the row tiles of a W column tile share an XCD
+    a.group_m = (pl.kind == Kind::Dec || pl.kind == Kind::Strip || pl.kind == Kind::WStrip) ? a.tiles_m : 4;
     a.act = p.act;
     a.out_f32 = p.out_f32 ? 1 : 0;
     a.eps = p.eps;
@@ -322,19 +347,47 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
         a.splits = (nk + per - 1) / per;
         a.kchunk = per * pl.bk;
     }
-    if (a.splits > 1) {
-        const size_t tiles = (size_t)a.tiles_m * a.tiles_n;
-        const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
-        const size_t acc_floats = nb * pl.bm * pl.bn;                      // per tile and split
-        const size_t ss_floats = (size_t)pl.threads() * (pl.bm / pl.wm / 32 / pl.kg);  // RMS partial sums
-        const size_t per_split = (pl.kind == Kind::Dec) ? 256 * 36 : (acc_floats + ss_floats) * sizeof(float);
-        if (tiles >= kCounterBytes / sizeof(unsigned)) return hipErrorInvalidValue;
-        hipError_t e = get_workspace(stream, tiles * a.splits * per_split, &a.ws, &a.cnt);
-        if (e != hipSuccess) return e;
-    }
+    return c;
+}
+
+// Bytes of fp32 partials a split call exchanges: per tile and split, the
+// accumulators of every operand and the RMS partial sums of squares (the
+// small-M kernel: 8 floats plus one sum per thread).
+size_t split_bytes(const Plan& pl, const Problem& p, const KArgs& a) {
+    const size_t tiles = (size_t)a.tiles_m * a.tiles_n;
+    const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
+    const size_t acc_floats = nb * pl.bm * pl.bn;
+    const size_t ss_floats = (size_t)pl.threads() * (pl.bm / pl.wm / 32 / pl.kg);
+    const size_t per_split = (pl.kind == Kind::Dec) ? 256 * 36 : (acc_floats + ss_floats) * sizeof(float);
+    return tiles * a.splits * per_split;
+}
+
+}  // namespace
+
+size_t workspace_bytes(const Problem& p) {
+    if (p.M == 0) return 0;
+    KArgs a;
+    const Choice c = setup(p, a);
+    if (a.splits == 1) return 0;
+    return kCounterBytes + split_bytes(*c.plan, p, a);
+}
+
+hipError_t launch(const Problem& p, hipStream_t stream) {
+    if (p.M == 0) return hipSuccess;
+    KArgs a;
+    const Choice c = setup(p, a);
+    const Plan& pl = *c.plan;
+    if (a.splits > 1 && (size_t)a.tiles_m * a.tiles_n >= kCounterBytes / sizeof(unsigned))
+        return hipErrorInvalidValue;
     const int nwg = a.tiles_m * a.tiles_n * a.splits;
     const void* fn = kernel_for((int)(c.plan - kPlans), p, a.splits > 1);
     if (fn == nullptr) return hipErrorInvalidDeviceFunction;
+    if (a.splits > 1) {
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        const hipError_t e = get_workspace(stream, split_bytes(pl, p, a), &a.ws, &a.cnt);
+        if (e != hipSuccess) return e;
+        return launch_fn(fn, a, nwg, pl.threads(), stream);
+    }
     return launch_fn(fn, a, nwg, pl.threads(), stream);
 }
 

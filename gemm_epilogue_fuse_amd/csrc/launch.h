@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace lf {
@@ -29,6 +30,10 @@ struct Problem {
 // Enqueue the kernel(s) for `p` on `stream`.  Returns hipSuccess or the
 // launch error.
 hipError_t launch(const Problem& p, hipStream_t stream);
+
+// Bytes of split-K workspace (partials and arrival counters) `launch` uses
+// for `p`; 0 when its plan does not split K.  No HIP call.
+size_t workspace_bytes(const Problem& p);
 
 // Name of the tile configuration `launch` would use for `p` (static string).
 const char* plan_name(const Problem& p);

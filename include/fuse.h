@@ -50,15 +50,23 @@
  *              keeps no pointer after the call returns.
  *  Workspace   Plans that split K across workgroups exchange float32 partial
  *              sums through a library-owned device buffer, one per (device,
- *              stream), allocated by the first call on that stream that needs
- *              it (at least 64 MiB plus 1 MiB of arrival counters) and kept
- *              until the process ends.  A call that needs a larger buffer
- *              first synchronises its stream, then frees and reallocates.
- *              Calls on one stream use it in stream order; calls on
- *              different streams never share it.  A call captured into a
- *              HIP graph must come after an eager call on the capturing
- *              stream that needed at least as much workspace: an allocation
- *              during capture fails with FUSE_E_HIP.
+ *              stream), allocated (hipMalloc) by the first call on that stream
+ *              that needs it: at least 64 MiB, including 1 MiB of arrival
+ *              counters, which a small kernel zeroes on the caller's stream.
+ *              fuse_workspace_bytes reports what a call needs; the automatic
+ *              plans stay within the 64 MiB minimum.  A call needing more than
+ *              the stream's buffer holds allocates a new one of at least twice
+ *              the size; the old buffer is kept (never freed before the process
+ *              ends), since a HIP graph captured earlier may still use it.
+ *              Calls on one stream use the buffer in stream order; calls on
+ *              different streams never share it.  A graph replay uses the
+ *              buffer of the stream it was captured on, so it must not run
+ *              concurrently with other split-K work from that stream.  A call
+ *              captured into a HIP graph must come after an eager call on the
+ *              capturing stream that needed at least as much workspace: an
+ *              allocation during capture fails with FUSE_E_HIP
+ *              (hipErrorStreamCaptureUnsupported).  This buffer and the plan
+ *              override of fuse_set_plan are the library's only state.
  *  Stream      `stream` is a hipStream_t (NULL: the default stream).  Calls are
  *              asynchronous: they return once the kernel is enqueued.
  *  Aliasing    Y must not overlap any input, except Y == residual exactly
@@ -158,6 +166,14 @@ int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
  */
 const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype);
 int fuse_set_plan(const char* name);
+
+/*
+ * Bytes of split-K workspace (float32 partials plus arrival counters) a call
+ * of entry point `op` (numbered as for fuse_plan_name) with these arguments
+ * uses under the current plan choice; 0 when its plan does not split K, -1
+ * for an unknown op, dtype or invalid shape.  No HIP call.
+ */
+int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fuse_strerror(int status);

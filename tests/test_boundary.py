@@ -210,3 +210,42 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         lf.rmsnorm_gemm(torch.zeros(4, 8, dtype=torch.bfloat16), torch.ones(8, dtype=torch.bfloat16),
                         torch.zeros(8, 8, dtype=torch.bfloat16))
+
+
+# --------------------------------------------------------------------------- split-K workspace sizing
+
+def test_workspace_bytes_sizing(L):
+    """The workspace a call needs follows from its plan: no split, no
+    workspace; a split call needs its arrival counters (1 MiB) plus one fp32
+    partial tile per tile and split (plus the RMS sums of squares); every
+    automatic plan fits the 64 MiB a stream's first buffer holds."""
+    MiB = 1 << 20
+    lf.set_plan(None)
+    # 4096^3: enough 256x256 tiles, no split
+    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.workspace_bytes(0, 4096, 4096, 4096) == 0
+    # 512x4096x4096 splits K two ways on 128x128 tiles: 128 tiles x 2 splits x
+    # (a 128x128 fp32 tile + one sum of squares per thread and owned row block)
+    assert lf.plan_name(0, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"
+    assert lf.workspace_bytes(0, 512, 4096, 4096) == MiB + 128 * 2 * (128 * 128 + 512 * 1) * 4
+    assert lf.workspace_bytes(1, 512, 4096, 4096) == lf.workspace_bytes(0, 512, 4096, 4096)
+    # decode shape: 32-row tiles, K chunks of 512, 9216 bytes per tile and chunk
+    assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"
+    assert lf.workspace_bytes(1, 1, 4096, 4096) == MiB + 64 * 8 * 256 * 36
+    # whole-strip few-row plan: no split
+    assert lf.workspace_bytes(1, 1, 1024, 1024) == 0
+    assert lf.workspace_bytes(0, 0, 4096, 4096) == 0
+    with pytest.raises(ValueError):
+        lf.workspace_bytes(0, 64, 12, 64)
+    with pytest.raises(ValueError):
+        lf.workspace_bytes(5, 64, 64, 64)
+    for op in (0, 1, 2):
+        for M in (1, 17, 32, 33, 128, 129, 512, 1024, 2048, 4096):
+            for N, K in ((1024, 1024), (4096, 4096), (11008, 4096), (4096, 11008), (2048, 8192)):
+                assert lf.workspace_bytes(op, M, N, K) <= 64 * MiB, (op, M, N, K)
+    # a forced plan with many splits can need more than the first buffer
+    lf.set_plan("dma_128x128x64_s4:k16")
+    try:
+        assert lf.workspace_bytes(0, 4096, 4096, 8192) == MiB + 32 * 32 * 16 * (128 * 128 + 256 * 2) * 4
+    finally:
+        lf.set_plan(None)
