@@ -1,23 +1,37 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused RMSNorm -> Linear / GEMM + epilogue kernels on one MI355X.
+"""Benchmark of the fused GEMM + epilogue and RMSNorm -> Linear kernels on one MI355X.
 
-Default run (one JSON line on stdout): the fused RMSNorm -> Linear workload
-X[512,4096] fp16 -> RMSNorm(gamma, eps=1e-6) -> . W[4096,4096], no bias, no
-activation ("LLMBoost", benchmark results: the [512,4096] x [4096,4096] fp16
-shape).  One step = one fused call over one batch of resident inputs.  The
-inputs rotate over enough independent sets that consecutive steps cannot hit
-in the 256 MB last-level cache (the layer-after-layer situation of a model).
+Default run: one JSON line on stdout.  Its headline is the fused RMSNorm ->
+Linear workload X[512,4096] fp16 -> RMSNorm(gamma, eps=1e-6) -> . W[4096,4096],
+no bias, no activation ("LLMBoost", benchmark results: the [512,4096] x
+[4096,4096] fp16 shape).  One step = one fused call over one batch of
+resident inputs.  ``workloads`` in the same line carries every other
+workload at its full size: the 64x256x256 GEMM + bias + GeLU, the GEMM +
+bias + activation sweep (M = 512..4096, N = K = 4096) with its SiLU, ReLU and
+residual variants, the bf16 SwiGLU FFN block (both kernels and their sum) and
+the decode-shaped RMSNorm -> Linear cells (B x D, fp16 and bf16).  Each
+carries its roofline fields and, beside it, the same computation unfused
+through torch (rms_norm, hipBLASLt matmul, separate elementwise kernels),
+timed the same way ("llm-fusion-compiler", benchmark table: generated kernel
+against the vendor library; "LLMBoost", benchmark results and speedup across
+shapes: unfused against fused).
 
-    python bench.py [--steps K] [--warmup W] [--sweep] [--no-cpu]
+Timing.  Every workload is timed as a HIP graph of back-to-back calls over
+enough independent input sets that consecutive calls cannot hit in the 256 MB
+last-level cache (the layer-after-layer situation of a model), replayed on
+one stream; wall clock and HIP events on that stream bracket the same replay.
+The headline's graph holds exactly --steps calls.
 
-``--sweep`` also prints one JSON line per extra workload to stderr (the
-GEMM + bias + activation sweep, the SwiGLU FFN block and the decode-shaped
-RMSNorm -> Linear cells).  ``--calibrate-copy`` runs a plain device copy of
-known size for scaling hardware traffic counters.
+    python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu] [--no-sweep]
+
+``--only`` keeps the workloads whose name contains NAME (for profiling one
+kernel at a time; the headline is always timed).  ``--calibrate-copy`` runs a
+plain device copy of known size for scaling hardware traffic counters.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,16 +49,15 @@ EPS = 1e-6
 # The pages' own figure for this exact workload: 0.208 ms fused on an NVIDIA A30
 # ("LLMBoost", benchmark results).  Context only (other hardware).
 PAGE_A30_MS = 0.208
+HEADLINE = "rmsnorm_linear_512x4096x4096_fp16"
 
-# Every device source compiled into libfuse: the stored HBM-traffic counters
-# are used only while these hash to the value recorded with them.
-KERNEL_SOURCES = ["gemm_epilogue_fuse_amd/csrc/gemm_fused.hip", "gemm_epilogue_fuse_amd/csrc/kernels.h",
-                  "gemm_epilogue_fuse_amd/csrc/k_dma_square.hip", "gemm_epilogue_fuse_amd/csrc/k_dma_wide.hip",
-                  "gemm_epilogue_fuse_amd/csrc/k_reg.hip", "gemm_epilogue_fuse_amd/csrc/k_small.hip",
-                  "gemm_epilogue_fuse_amd/csrc/kernel_dma.h",
-                  "gemm_epilogue_fuse_amd/csrc/kernel_reg.h", "gemm_epilogue_fuse_amd/csrc/common.h",
-                  "gemm_epilogue_fuse_amd/csrc/kernel_decode.h", "gemm_epilogue_fuse_amd/csrc/kernel_strip.h",
-                  "gemm_epilogue_fuse_amd/csrc/launch.h"]
+# Every device source compiled into libfuse: the stored hardware-counter
+# summaries are used only while these hash to the value recorded with them.
+CSRC = "gemm_epilogue_fuse_amd/csrc/"
+KERNEL_SOURCES = [CSRC + f for f in (
+    "gemm_fused.hip", "kernels.h", "k_dma_square.hip", "k_dma_wide.hip", "k_reg.hip", "k_small.hip",
+    "kernel_dma.h", "kernel_reg.h", "common.h", "kernel_decode.h", "kernel_strip.h", "kernel_wstrip.h",
+    "launch.h")]
 
 
 def kernel_hash() -> str:
@@ -61,139 +74,72 @@ def log(*a):
 
 # ----------------------------------------------------------------------------- timing
 
-# Untimed launches before the warmup steps, long enough for the GPU clocks to
+# Untimed launches before the timed replay, long enough for the GPU clocks to
 # leave their idle state (a few ms of launches after an idle host phase
 # measured about 10% slow).
 SETTLE_S = 0.3
 
 
-def time_calls(fn_for_set, nsets, steps, warmup, settle_s=None):
-    """Run fn_for_set(i % nsets) for settle_s seconds, then warmup + steps
-    times.  Returns (wall ms/step, device ms per launch): HIP events on the
-    launching stream bracket the whole batch of back-to-back launches, so
-    short kernels are not charged for the host's gap between calls."""
+def capture(calls, stream):
+    """A HIP graph of calls[i](stream) for every i, captured on `stream`."""
     import torch
-    t_end = time.perf_counter() + (SETTLE_S if settle_s is None else settle_s)
-    i = 0
-    while time.perf_counter() < t_end:
-        for _ in range(16):
-            fn_for_set(i % nsets)
-            i += 1
-        torch.cuda.synchronize()
-    for i in range(warmup):
-        fn_for_set(i % nsets)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(steps):
-        fn_for_set(i % nsets)
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    dev_ms = e0.elapsed_time(e1) / steps
-    return wall_ms, dev_ms
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c(stream)
+    return g
 
 
-def launch_floor_us(steps=200, graph=False):
-    """Device time per launch of a one-element device op, timed like the
-    kernels (eager, or by HIP-graph replay): the floor under any call's
-    latency."""
-    import torch
-    x = torch.zeros(1, device="cuda:0")
-    if graph:
-        return round(graph_time_ms(lambda i, strm: x.add_(1.0), 1) * 1e3, 3)
-    _, dev = time_calls(lambda i: x.add_(1.0), 1, steps, 20)
-    return round(dev * 1e3, 3)
+def time_graph(call_on, nsets, launches, warmup, settle_s=None, replays=1):
+    """Time `launches` calls call_on(i % nsets, stream) captured in one HIP graph.
 
-
-def rotating_sets(make, bytes_per_set):
-    n = max(2, min(64, (ROTATE_BYTES + bytes_per_set - 1) // bytes_per_set))
-    return [make(i) for i in range(n)]
-
-
-# ----------------------------------------------------------------------------- workloads
-
-def rms_linear_sets(M, D, N, dtype_s, seed=0, order=("X", "gamma", "W")):
-    import synth
-    d = synth.rmsnorm_linear(M=M, D=D, N=N, seed=seed, dtype=dtype_s, order=order,
-                             w_std=1.0 / (D ** 0.5))
-    base = {k: synth.to_torch(v, dtype_s, "cuda:0") for k, v in d.items()}
-    per_set = (M * D + D + D * N + M * N) * 2
-
-    def make(i):
-        if i == 0:
-            t = dict(base)
-        else:
-            t = {k: v.clone() for k, v in base.items()}
-        t["Y"] = torch_empty((M, N), base["X"].dtype)
-        return t
-    return d, rotating_sets(make, per_set)
-
-
-def torch_empty(shape, dtype):
-    import torch
-    return torch.empty(shape, dtype=dtype, device="cuda:0")
-
-
-def bench_rms_linear(M, D, N, dtype_s, steps, warmup, order=("X", "gamma", "W"), graph=False):
-    """Time fuse_rmsnorm_gemm through the C ABI with pre-marshalled pointers
-    (what a native caller does), so host-side Python cost stays out of the way."""
-    import ctypes
-    import torch
-    import gemm_epilogue_fuse_amd as lf
-    d, sets = rms_linear_sets(M, D, N, dtype_s, order=order)
-    L = lf.lib()
-    code = lf.BF16 if dtype_s == "bf16" else lf.F16
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    eps = ctypes.c_float(EPS)
-    argv = [(s["X"].data_ptr(), s["gamma"].data_ptr(), s["W"].data_ptr(), s["Y"].data_ptr()) for s in sets]
-    fn = L.fuse_rmsnorm_gemm
-
-    def call_on(i, strm):
-        x, g, w, y = argv[i]
-        rc = fn(x, g, eps, w, None, y, M, N, D, 0, code, strm)
-        if rc:
-            raise lf.FuseError(rc, "fuse_rmsnorm_gemm")
-
-    def call(i):
-        call_on(i, stream)
-    wall, dev = time_calls(call, len(sets), steps, warmup)
-    flops = 2.0 * M * N * D
-    alg_bytes = (M * D + D + D * N + M * N) * 2
-    if graph:
-        gdev = graph_time_ms(call_on, len(sets))
-        return d, sets, wall, dev, flops, alg_bytes, gdev
-    return d, sets, wall, dev, flops, alg_bytes
-
-
-def graph_time_ms(call_on, nsets, launches=40, replays=10):
-    """Device ms per launch from a HIP graph of `launches` back-to-back calls
-    over the rotating input sets, replayed `replays` times: no host launch
-    gap between kernels, so short calls show their device time."""
-    import ctypes
+    The calls first run eagerly (settle_s seconds, then `warmup` more), which
+    also creates any per-stream library state before capture.  Then the graph
+    is replayed `replays` times, bracketed by torch.cuda.synchronize(), a wall
+    clock and HIP events recorded on the replay stream.  Returns (wall ms per
+    call, event ms per call)."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    sp = ctypes.c_void_p(s.cuda_stream)
+    t_end = time.perf_counter() + (SETTLE_S if settle_s is None else settle_s)
+    i = 0
     with torch.cuda.stream(s):
-        for i in range(nsets):  # per-stream library state (split-K workspace) exists before capture
-            call_on(i, sp)
-    s.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for i in range(launches):
-            call_on(i % nsets, sp)
+        while True:
+            for _ in range(max(warmup, nsets)):
+                call_on(i % nsets, s)
+                i += 1
+            s.synchronize()
+            if time.perf_counter() >= t_end:
+                break
+    g = capture([(lambda st, j=j: call_on(j % nsets, st)) for j in range(launches)], s)
     with torch.cuda.stream(s):
-        for _ in range(3):
-            g.replay()
+        g.replay()  # the first replay uploads the graph
+        s.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(s)
         for _ in range(replays):
             g.replay()
-        e1.record()
-    s.synchronize()
-    return e0.elapsed_time(e1) / (launches * replays)
+        e1.record(s)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / (launches * replays)
+    dev = e0.elapsed_time(e1) / (launches * replays)
+    del g
+    return wall, dev
+
+
+def launch_floor_us(launches=200):
+    """Device time per call of a one-element device op in a replayed HIP graph:
+    the floor under any call's latency."""
+    import torch
+    x = torch.zeros(1, device="cuda:0")
+    _, dev = time_graph(lambda i, st: x.add_(1.0), 1, launches, 20, settle_s=0.0, replays=5)
+    return round(dev * 1e3, 3)
+
+
+def n_sets(bytes_per_set):
+    return max(2, min(64, (ROTATE_BYTES + bytes_per_set - 1) // bytes_per_set))
 
 
 def result_fields(dev_ms, flops, alg_bytes):
@@ -216,8 +162,9 @@ def result_fields(dev_ms, flops, alg_bytes):
 # ----------------------------------------------------------------------------- traffic counters
 
 def read_traffic(name):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    or None if absent or taken on a different kernel source."""
+    """Bytes per launch between the L2 and the memory fabric (L2 misses, served
+    by the last-level cache or HBM) from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -231,7 +178,7 @@ def read_traffic(name):
     if vals.get("kernel_source_sha256_16") != kernel_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["l2_fabric_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -239,7 +186,7 @@ def read_traffic(name):
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(min_seconds=10.0):
-    """The fp64 oracle, as it stands, on the same workload (whole 512x4096x4096
+    """The fp64 oracle, as it stands, on the headline workload (whole 512x4096x4096
     problem, repeated until ~min_seconds of CPU work), in TFLOP/s."""
     import numpy as np
     import oracle
@@ -263,131 +210,229 @@ def cpu_baseline(min_seconds=10.0):
                       % (reps, per)}
 
 
-# ----------------------------------------------------------------------------- sweep
+# ----------------------------------------------------------------------------- workloads
+#
+# A workload: its inputs (drawn once with the seeded generators, then cloned
+# into rotating sets on the device), the fused call through the C ABI with
+# pre-marshalled pointers (what a native caller does), and the same
+# computation unfused through torch.
 
-def sweep(steps, warmup, only=None):
-    """One JSON line per workload on stderr; `only` keeps the workloads whose
-    name contains it (for profiling one kernel at a time)."""
-    import torch
-    import gemm_epilogue_fuse_amd as lf
+class Workload:
+    def __init__(self, name, dtype, flops, alg_bytes, make, fused, unfused, plan, extra=None):
+        self.name, self.dtype, self.flops, self.alg_bytes = name, dtype, flops, alg_bytes
+        self.make, self.fused, self.unfused, self.plan = make, fused, unfused, plan
+        self.extra = extra or {}
+
+
+def _dev(bits, dt):
     import synth
+    return synth.to_torch(bits, dt, "cuda:0")
 
-    def emit(rec):
-        print(json.dumps(rec), file=sys.stderr, flush=True)
 
-    def want(name):
-        return only is None or only in name
+def _sets(base, bytes_per_set, outputs):
+    """Rotating input sets: set 0 is `base`, the others device clones; each set
+    gets its own output buffers from outputs()."""
+    sets = []
+    for i in range(n_sets(bytes_per_set)):
+        t = dict(base) if i == 0 else {k: v.clone() for k, v in base.items()}
+        t.update(outputs())
+        sets.append(t)
+    return sets
 
-    # GEMM + bias + activation, N = K = 4096
+
+def _code(lf, dt):
+    import synth
+    return lf.BF16 if dt == synth.BF16 else lf.F16
+
+
+def gemm_workload(lf, name, M, N, K, act, resid, dt, draw):
+    import torch
+    import torch.nn.functional as F
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    alg = (M * K + K * N + N + M * N * (2 if resid else 1)) * 2
+    code = _code(lf, dt)
+    L = lf.lib()
+    actc = lf.ACT[act]
+
+    def make():
+        d = draw()
+        base = {k: _dev(v, dt) for k, v in d.items()}
+        return _sets(base, alg, lambda: {"Y": torch.empty((M, N), dtype=tdt, device="cuda:0")})
+
+    def fused(s):
+        args = (s["A"].data_ptr(), s["W"].data_ptr(), s["bias"].data_ptr(),
+                s["R"].data_ptr() if resid else None, s["Y"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_gemm_epilogue(*args, M, N, K, actc, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_gemm_epilogue")
+        return call
+
+    def unfused(s):
+        A, W, b = s["A"], s["W"], s["bias"]
+        R = s.get("R")
+
+        def call(st):
+            z = torch.addmm(b, A, W)
+            if act == "gelu_tanh":
+                z = F.gelu(z, approximate="tanh")
+            elif act == "silu":
+                z = F.silu(z)
+            elif act == "relu":
+                z = F.relu(z)
+            if R is not None:
+                z = z + R
+            return z
+        return call
+    return Workload(name, dt, 2.0 * M * N * K, alg, make, fused, unfused, lf.plan_name(0, M, N, K, code))
+
+
+def rms_workload(lf, name, M, D, N, dt, draw):
+    import torch
+    import torch.nn.functional as F
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    alg = (M * D + D + D * N + M * N) * 2
+    code = _code(lf, dt)
+    L = lf.lib()
+    eps = ctypes.c_float(EPS)
+
+    def make():
+        d = draw()
+        base = {k: _dev(v, dt) for k, v in d.items()}
+        return _sets(base, alg, lambda: {"Y": torch.empty((M, N), dtype=tdt, device="cuda:0")})
+
+    def fused(s):
+        args = (s["X"].data_ptr(), s["gamma"].data_ptr(), eps, s["W"].data_ptr(), None, s["Y"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_rmsnorm_gemm(*args, M, N, D, 0, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_rmsnorm_gemm")
+        return call
+
+    def unfused(s):
+        X, g, W = s["X"], s["gamma"], s["W"]
+        return lambda st: torch.matmul(F.rms_norm(X, (D,), g, EPS), W)
+    return Workload(name, dt, 2.0 * M * N * D, alg, make, fused, unfused, lf.plan_name(1, M, N, D, code))
+
+
+def swiglu_workloads(lf, M, D, F_):
+    """The bf16 SwiGLU FFN block as its two fused kernels, and their sum."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    L = lf.lib()
+    code = lf.BF16
+    eps = ctypes.c_float(EPS)
+    b1 = (M * D + D + 2 * D * F_ + M * F_) * 2
+    b2 = (M * F_ + F_ * D + D + 2 * M * D) * 2
+    shared = {}
+
+    def make():
+        if "sets" not in shared:
+            d = synth.swiglu_ffn(M=M, D=D, F=F_, seed=0)
+            base = {k: _dev(v, synth.BF16) for k, v in d.items()}
+            shared["sets"] = _sets(base, b1 + b2, lambda: {
+                "H": torch.empty((M, F_), dtype=torch.bfloat16, device="cuda:0"),
+                "Y": torch.empty((M, D), dtype=torch.bfloat16, device="cuda:0")})
+        return shared["sets"]
+
+    def k1(s):
+        a = (s["X"].data_ptr(), s["gamma"].data_ptr(), eps, s["Wg"].data_ptr(), s["Wu"].data_ptr(),
+             s["H"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_rmsnorm_gemm_swiglu(*a, M, F_, D, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_rmsnorm_gemm_swiglu")
+        return call
+
+    def k2(s):
+        a = (s["H"].data_ptr(), s["Wd"].data_ptr(), s["bias"].data_ptr(), s["X"].data_ptr(), s["Y"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_gemm_epilogue(*a, M, D, F_, 0, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_gemm_epilogue")
+        return call
+
+    def block(s):
+        c1, c2 = k1(s), k2(s)
+
+        def call(st):
+            c1(st)
+            c2(st)
+        return call
+
+    def u1(s):
+        X, g, Wg, Wu = s["X"], s["gamma"], s["Wg"], s["Wu"]
+
+        def call(st):
+            xn = F.rms_norm(X, (D,), g, EPS)
+            return F.silu(torch.matmul(xn, Wg)) * torch.matmul(xn, Wu)
+        return call
+
+    def u2(s):
+        H, Wd, b, X = s["H"], s["Wd"], s["bias"], s["X"]
+        return lambda st: torch.addmm(b, H, Wd) + X
+
+    def ub(s):
+        c1, c2 = u1(s), u2(s)
+        Wd, b, X = s["Wd"], s["bias"], s["X"]
+        return lambda st: torch.addmm(b, c1(st), Wd) + X
+
+    f1, f2 = 4.0 * M * F_ * D, 2.0 * M * D * F_
+    return [
+        Workload("swiglu_k1_rmsnorm_gate_up_%dx%dx%d_bf16" % (M, F_, D), "bf16", f1, b1, make, k1, u1,
+                 lf.plan_name(2, M, F_, D, code)),
+        Workload("swiglu_k2_down_bias_residual_%dx%dx%d_bf16" % (M, D, F_), "bf16", f2, b2, make, k2, u2,
+                 lf.plan_name(0, M, D, F_, code)),
+        Workload("swiglu_ffn_block_%dx%dx%d_bf16" % (M, D, F_), "bf16", f1 + f2, b1 + b2, make, block, ub,
+                 lf.plan_name(2, M, F_, D, code) + " + " + lf.plan_name(0, M, D, F_, code)),
+    ]
+
+
+def all_workloads(lf):
+    import synth
+    ws = [gemm_workload(lf, "gemm_bias_gelu_tanh_64x256x256_fp16", 64, 256, 256, "gelu_tanh", False, "f16",
+                        lambda: synth.gemm_bias_gelu_small(seed=0))]
     for M, act, resid in [(512, "gelu_tanh", False), (1024, "gelu_tanh", False), (2048, "gelu_tanh", False),
                           (4096, "gelu_tanh", False), (4096, "silu", False), (4096, "relu", False),
                           (4096, "none", True)]:
-        N = K = 4096
-        name = "gemm_bias_%s%s_%dx4096x4096_fp16" % (act, "_residual" if resid else "", M)
-        if not want(name):
-            continue
-        d = synth.gemm_epilogue_sweep(M, N, K, seed=0, residual=resid)
-        base = {k: synth.to_torch(v, synth.F16, "cuda:0") for k, v in d.items()}
-        per = (M * K + K * N + N + M * N * (2 if resid else 1)) * 2
-
-        def make(i, base=base, M=M, N=N):
-            t = base if i == 0 else {k: v.clone() for k, v in base.items()}
-            t = dict(t)
-            t["Y"] = torch.empty((M, N), dtype=torch.float16, device="cuda:0")
-            return t
-        sets = rotating_sets(make, per)
-
-        def call(i, sets=sets, act=act):
-            s = sets[i]
-            lf.gemm_epilogue(s["A"], s["W"], s["bias"], s.get("R"), act, out=s["Y"])
-        _, dev = time_calls(call, len(sets), steps, warmup)
-        rec = {"workload": name, "plan": lf.plan_name(0, M, N, K)}
-        rec.update(result_fields(dev, 2.0 * M * N * K, per))
-        emit(rec)
-        del sets, base
-
-    # The same work unfused through the vendor library, for context: torch's
-    # rms_norm, matmul (hipBLASLt) and elementwise kernels, timed the same way
-    # (warm inputs: one set).
-    def unfused(name, fn, flops, alg):
-        if not want(name):
-            return
-        _, dev = time_calls(lambda i: fn(), 1, steps, warmup)
-        rec = {"workload": name, "plan": "torch (hipBLASLt matmul + separate elementwise kernels)"}
-        rec.update(result_fields(dev, flops, alg))
-        emit(rec)
-
-    F = torch.nn.functional
-    X = torch.randn(512, 4096, device="cuda:0").half()
-    g = (1 + 0.1 * torch.randn(4096, device="cuda:0")).half()
-    W = (torch.randn(4096, 4096, device="cuda:0") / 64).half()
-    unfused("unfused_rmsnorm_then_matmul_512x4096x4096_fp16",
-            lambda: torch.matmul(F.rms_norm(X, (4096,), g, EPS), W),
-            2.0 * 512 * 4096 * 4096, (2 * 512 * 4096 + 4096 + 4096 * 4096) * 2)
-    A = torch.randn(4096, 4096, device="cuda:0").half()
-    bias = (0.1 * torch.randn(4096, device="cuda:0")).half()
-    unfused("unfused_matmul_bias_gelu_tanh_4096x4096x4096_fp16",
-            lambda: F.gelu(torch.matmul(A, W) + bias, approximate="tanh"),
-            2.0 * 4096 ** 3, (3 * 4096 * 4096 + 4096) * 2)
-    del X, g, W, A, bias
-
-    # SwiGLU FFN block, bf16: kernel 1 (RMSNorm + gate/up + SiLU*up), kernel 2 (down + bias + residual)
-    M, D, F = 2048, 4096, 11008
-    n1 = "swiglu_k1_rmsnorm_gate_up_2048x11008x4096_bf16"
-    n2 = "swiglu_k2_down_bias_residual_2048x4096x11008_bf16"
-    n3 = "swiglu_ffn_block_bf16_total"
-    if want(n1) or want(n2) or want(n3):
-        swiglu_block(lf, synth, emit, steps, warmup, M, D, F, n1, n2, n3)
-
-    # decode-shaped RMSNorm -> Linear, timed by HIP-graph replay (eager
-    # launches of a few-microsecond kernel measure the host's launch rate);
-    # cells whose roofline time is under the launch floor cannot show their
-    # HBM fraction and are flagged
-    floor = launch_floor_us(graph=True)
-    if want("launch_floor_one_element_op"):
-        emit({"workload": "launch_floor_one_element_op", "latency_us": floor,
-              "timing": "HIP graph of 40 launches, replayed", "eager_latency_us": launch_floor_us()})
+        name = "gemm_bias_%s%s_%dx4096x4096_fp16" % ("residual" if resid else act, "", M)
+        ws.append(gemm_workload(lf, name, M, 4096, 4096, act, resid, "f16",
+                                lambda M=M, resid=resid: synth.gemm_epilogue_sweep(M, seed=0, residual=resid)))
+    ws += swiglu_workloads(lf, 2048, 4096, 11008)
     for dt in (synth.F16, synth.BF16):
         for D in (1024, 2048, 4096):
             for B in (1, 32, 128, 512, 1024):
-                name = "decode_rmsnorm_linear_B%d_D%d_%s" % (B, D, dt)
-                if not want(name):
-                    continue
-                _, sets, _, dev, flops, alg, gdev = bench_rms_linear(B, D, D, dt, steps, warmup,
-                                                                     order=("W", "X", "gamma"), graph=True)
-                rec = {"workload": name,
-                       "plan": lf.plan_name(1, B, D, D, lf.BF16 if dt == synth.BF16 else lf.F16),
-                       "timing": "HIP graph of 40 launches, replayed"}
-                rec.update(result_fields(gdev, flops, alg))
-                rec["eager_latency_us"] = round(dev * 1e3, 3)
-                rec["launch_floor_us"] = floor
-                rec["below_launch_floor"] = rec["roof_us"] < floor
-                emit(rec)
-                del sets
+                ws.append(rms_workload(lf, "decode_rmsnorm_linear_B%d_D%d_%s" % (B, D, dt), B, D, D, dt,
+                                       lambda B=B, D=D, dt=dt: synth.decode_rmsnorm_linear(B, D, seed=0, dtype=dt)))
+                ws[-1].extra["decode"] = True
+    return ws
 
 
-def swiglu_block(lf, synth, emit, steps, warmup, M, D, F, n1, n2, n3):
-    """SwiGLU FFN block in bf16: kernel 1 (RMSNorm + gate/up + SiLU*up) and
-    kernel 2 (down + bias + residual)."""
-    import torch
-    d = synth.swiglu_ffn(M=M, D=D, F=F, seed=0)
-    t = {k: synth.to_torch(v, synth.BF16, "cuda:0") for k, v in d.items()}
-    H = torch.empty((M, F), dtype=torch.bfloat16, device="cuda:0")
-    Y = torch.empty((M, D), dtype=torch.bfloat16, device="cuda:0")
-    _, dev1 = time_calls(lambda i: lf.rmsnorm_gemm_swiglu(t["X"], t["gamma"], t["Wg"], t["Wu"], EPS, out=H),
-                         1, steps, warmup)
-    _, dev2 = time_calls(lambda i: lf.gemm_epilogue(H, t["Wd"], t["bias"], t["X"], "none", out=Y), 1, steps, warmup)
-    b1 = (M * D + D + 2 * D * F + M * F) * 2
-    b2 = (M * F + F * D + D + 2 * M * D) * 2
-    r1 = {"workload": n1, "plan": lf.plan_name(2, M, F, D, lf.BF16)}
-    r1.update(result_fields(dev1, 4.0 * M * F * D, b1))
-    emit(r1)
-    r2 = {"workload": n2, "plan": lf.plan_name(0, M, D, F, lf.BF16)}
-    r2.update(result_fields(dev2, 2.0 * M * D * F, b2))
-    emit(r2)
-    r3 = {"workload": n3}
-    r3.update(result_fields(dev1 + dev2, 4.0 * M * F * D + 2.0 * M * D * F, b1 + b2))
-    emit(r3)
+def measure(w, launches=40, warmup=5, floor=None):
+    """Fused and unfused timings of one workload, as one record."""
+    sets = w.make()
+    fused = [w.fused(s) for s in sets]
+    unfused = [w.unfused(s) for s in sets]
+    nl = max(launches, len(sets))
+    _, dev = time_graph(lambda i, st: fused[i](st), len(sets), nl, warmup, settle_s=0.05, replays=2)
+    _, udev = time_graph(lambda i, st: unfused[i](st), len(sets), nl, warmup, settle_s=0.02, replays=2)
+    rec = {"workload": w.name, "dtype": w.dtype, "plan": w.plan}
+    rec.update(result_fields(dev, w.flops, w.alg_bytes))
+    rec["unfused_latency_us"] = round(udev * 1e3, 3)
+    rec["unfused"] = "torch: rms_norm / addmm and matmul (hipBLASLt) / separate elementwise kernels"
+    rec["speedup_vs_unfused"] = round(udev / dev, 3)
+    rec["rotating_input_sets"] = len(sets)
+    if w.extra.get("decode") and floor is not None:
+        rec["launch_floor_us"] = floor
+        rec["below_launch_floor"] = rec["roof_us"] < floor
+        rec["hbm_frac_cap"] = round(min(1.0, (w.alg_bytes / (PEAK_HBM_GBS * 1e9)) /
+                                        max(w.flops / (PEAK_MFMA_TFLOPS * 1e12), w.alg_bytes / (PEAK_HBM_GBS * 1e9))), 4)
+    return rec
 
 
 # ----------------------------------------------------------------------------- main
@@ -398,12 +443,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", default=None, help="with --sweep: only the workloads whose name contains this")
+    ap.add_argument("--only", default=None, help="only the extra workloads whose name contains this")
+    ap.add_argument("--no-sweep", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
-                    help="seconds of untimed launches before the warmup steps (0 under counter runs)")
+                    help="seconds of untimed launches before the headline's timed replay (0 under counter runs)")
     args = ap.parse_args()
     SETTLE_S = max(0.0, args.settle)
 
@@ -414,6 +459,7 @@ def main():
 
     import torch
     import gemm_epilogue_fuse_amd as lf
+    import synth
     if not os.path.exists(lf.LIB_PATH):
         from gemm_epilogue_fuse_amd import build
         build.build()
@@ -431,11 +477,15 @@ def main():
         log("calibration copy: %d bytes read + %d bytes written per launch, 5 launches" % (n, n))
         return
 
+    # ---- headline: exactly --steps calls in one graph, replayed once
     M, D, N = 512, 4096, 4096
-    d, sets, wall_ms, dev_ms, flops, alg = bench_rms_linear(M, D, N, "f16", args.steps, args.warmup)
-    fields = result_fields(dev_ms, flops, alg)
-    value = flops / (wall_ms * 1e-3) / 1e12       # whole-job throughput over the timed region
-    plan = lf.plan_name(1, M, N, D)
+    hw = rms_workload(lf, HEADLINE, M, D, N, synth.F16,
+                      lambda: synth.rmsnorm_linear(M=M, D=D, N=N, seed=0))
+    sets = hw.make()
+    calls = [hw.fused(s) for s in sets]
+    wall_ms, dev_ms = time_graph(lambda i, st: calls[i](st), len(sets), args.steps, args.warmup)
+    fields = result_fields(dev_ms, hw.flops, hw.alg_bytes)
+    value = hw.flops / (wall_ms * 1e-3) / 1e12       # whole-job throughput over the timed region
     traffic = read_traffic("rmsnorm_linear_512x4096x4096_fp16.traffic.txt")
     rec = {
         "metric": METRIC,
@@ -450,28 +500,47 @@ def main():
         "vs_baseline": round(PAGE_A30_MS / wall_ms, 3),
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "rmsnorm_linear_512x4096x4096_fp16", "M": M, "K": D, "N": N, "eps": EPS,
-                   "bias": None, "act": "none", "seed": 0, "plan": plan, "rotating_input_sets": len(sets),
-                   "clock_settle_s": SETTLE_S, "parallelism": "none (1 GPU)"},
+        "config": {"workload": HEADLINE, "M": M, "K": D, "N": N, "eps": EPS, "bias": None, "act": "none",
+                   "seed": 0, "plan": hw.plan, "rotating_input_sets": len(sets), "clock_settle_s": SETTLE_S,
+                   "parallelism": "none (1 GPU)"},
+        "timing": "one HIP graph of exactly `steps` calls over the rotating input sets, replayed once; "
+                  "value and ms_per_step from the wall clock, roofline from HIP events on the replay stream, "
+                  "both around that same replay",
         "latency_us": fields["latency_us"],
         "hbm_gbs": fields["hbm_gbs"],
         "mfma_frac": fields["mfma_frac"],
         "hbm_frac": fields["hbm_frac"],
         "roofline": {"bound": "mfma", "achieved": fields["tflops"], "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": fields["mfma_frac"], "traffic": traffic,
-                     "algorithmic_bytes": alg, "kernel": "%s (plan %s)" % ("gemm_dma_kernel" if plan.startswith("dma") else "gemm_fused_kernel", plan),
+                     "algorithmic_bytes": hw.alg_bytes, "algorithmic_flops": hw.flops,
+                     "kernel": "gemm_dma_kernel (plan %s)" % hw.plan,
                      "kernel_source_sha256_16": kernel_hash()},
-        "baseline_context": "0.208 ms fused on an NVIDIA A30 (page figure, other hardware); vs_baseline = 0.208 ms / ms_per_step",
+        "baseline_context": "0.208 ms fused on an NVIDIA A30 (page figure, other hardware); "
+                            "vs_baseline = 0.208 ms / ms_per_step",
     }
-    del sets
+    del calls, sets
+    log("headline: %.3f us per call (events), %.3f us (wall)" % (dev_ms * 1e3, wall_ms * 1e3))
+
+    # ---- every other workload, fused and unfused
+    if not args.no_sweep:
+        floor = launch_floor_us()
+        rec["launch_floor_us"] = floor
+        out = []
+        for w in all_workloads(lf):
+            if args.only is not None and args.only not in w.name:
+                continue
+            r = measure(w, floor=floor)
+            log(json.dumps(r))
+            out.append(r)
+            torch.cuda.empty_cache()
+        rec["workloads"] = out
+
     if not args.no_cpu:
         log("timing the fp64 oracle on the host cores ...")
         rec["cpu_baseline"] = cpu_baseline()
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)
-    if args.sweep:
-        sweep(max(20, args.steps // 4), max(5, args.warmup // 2), args.only)
 
 
 if __name__ == "__main__":

@@ -49,3 +49,24 @@ def test_traffic_counters_follow_the_kernel_sources(monkeypatch):
     monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
     assert bench.read_traffic(name) is None
     assert bench.read_traffic("no_such_summary.txt") is None
+
+
+def test_kernel_sources_cover_every_device_source():
+    """The counter-validity hash covers every file compiled into libfuse's kernels."""
+    csrc = os.path.join(ROOT, "gemm_epilogue_fuse_amd", "csrc")
+    device = sorted("gemm_epilogue_fuse_amd/csrc/" + f for f in os.listdir(csrc) if f.endswith((".h", ".hip")))
+    assert sorted(bench.KERNEL_SOURCES) == device
+
+
+def test_workload_list_covers_every_config():
+    """The default run times every workload of the operator's configuration list."""
+    import gemm_epilogue_fuse_amd as lf
+    names = [w.name for w in bench.all_workloads(lf)]
+    assert "gemm_bias_gelu_tanh_64x256x256_fp16" in names
+    for M in (512, 1024, 2048, 4096):
+        assert "gemm_bias_gelu_tanh_%dx4096x4096_fp16" % M in names
+    for v in ("silu", "relu", "residual"):
+        assert "gemm_bias_%s_4096x4096x4096_fp16" % v in names
+    assert sum(n.startswith("swiglu_") for n in names) == 3
+    dec = [n for n in names if n.startswith("decode_rmsnorm_linear_")]
+    assert len(dec) == 30 and len(set(dec)) == 30
