@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.fuse_gemm_epilogue.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.fuse_rmsnorm_gemm.restype = ci
         L.fuse_rmsnorm_gemm.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.fuse_rmsnorm_gemm_noalloc.restype = ci
+        L.fuse_rmsnorm_gemm_noalloc.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.fuse_rmsnorm_gemm_swiglu.restype = ci
         L.fuse_rmsnorm_gemm_swiglu.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, vp]
         L.fuse_plan_name.restype = ctypes.c_char_p
@@ -158,8 +160,11 @@ def gemm_epilogue(A, W, bias=None, residual=None, act="none", out=None, out_dtyp
     return Y
 
 
-def rmsnorm_gemm(X, gamma, W, eps=1e-6, bias=None, act="none", out=None, out_dtype=None):
-    """Y = act(RMSNorm_{gamma,eps}(X) @ W + bias); the normalised X stays on chip."""
+def rmsnorm_gemm(X, gamma, W, eps=1e-6, bias=None, act="none", out=None, out_dtype=None, noalloc=False):
+    """Y = act(RMSNorm_{gamma,eps}(X) @ W + bias); the normalised X stays on chip.
+
+    ``noalloc=True`` calls fuse_rmsnorm_gemm_noalloc (no device allocation by
+    the library; pass ``out`` too, so that nothing is allocated here either)."""
     torch = _torch()
     M, K = X.shape
     N = W.shape[1]
@@ -168,10 +173,11 @@ def rmsnorm_gemm(X, gamma, W, eps=1e-6, bias=None, act="none", out=None, out_dty
     _check(bias, "bias", X.dtype, (N,), X.device)
     code = _dtype_code(X, out_dtype)
     Y = _out(out, (M, N), torch.float32 if code & OUT_F32 else X.dtype, X.device)
-    rc = lib().fuse_rmsnorm_gemm(_ptr(X), _ptr(gamma), float(eps), _ptr(W), _ptr(bias), _ptr(Y),
-                                 M, N, K, _act(act), code, _stream(X.device))
+    fn = lib().fuse_rmsnorm_gemm_noalloc if noalloc else lib().fuse_rmsnorm_gemm
+    rc = fn(_ptr(X), _ptr(gamma), float(eps), _ptr(W), _ptr(bias), _ptr(Y), M, N, K, _act(act), code,
+            _stream(X.device))
     if rc != 0:
-        raise FuseError(rc, "fuse_rmsnorm_gemm")
+        raise FuseError(rc, "fuse_rmsnorm_gemm_noalloc" if noalloc else "fuse_rmsnorm_gemm")
     return Y
 
 

@@ -16,6 +16,8 @@
 
 namespace {
 
+static_assert(lf::kScratchBytes == FUSE_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
 // Per tensor: byte offsets of 16-bit elements, plus a K step and the
 // out-of-range bit, must stay below 2^32 (buffer offsets are 32-bit).
 constexpr int64_t kMaxElems = int64_t(1) << 29;
@@ -54,14 +56,48 @@ int check_eps(float eps) {
 
 thread_local int t_last_hip = 0;
 
-int run(const lf::Problem& p, void* stream) {
+int run(const lf::Problem& p, void* stream, bool noalloc = false) {
     if (p.M == 0) return FUSE_OK;
-    const hipError_t e = lf::launch(p, static_cast<hipStream_t>(stream));
+    const hipError_t e = lf::launch(p, static_cast<hipStream_t>(stream), noalloc);
     if (e != hipSuccess) {
         t_last_hip = static_cast<int>(e);
         return FUSE_E_HIP;
     }
     return FUSE_OK;
+}
+
+// fuse_rmsnorm_gemm and its allocation-free variant: checks, then launch.
+int rmsnorm_gemm(const void* X, const void* gamma, float eps, const void* W, const void* bias, void* Y,
+                 int64_t M, int64_t N, int64_t K, int act, int dtype, void* stream, bool noalloc) {
+    if (!gamma || !W || (M > 0 && (!X || !Y))) return FUSE_E_NULL;
+    bool bf16 = false, out_f32 = false;
+    if (int rc = check_dtype(dtype, &bf16, &out_f32)) return rc;
+    if (act < FUSE_ACT_NONE || act > FUSE_ACT_SILU) return FUSE_E_ENUM;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (int rc = check_eps(eps)) return rc;
+    if (!aligned16(X) || !aligned16(gamma) || !aligned16(W) || !aligned16(Y) ||
+        (bias && !aligned16(bias)))
+        return FUSE_E_ALIGN;
+    const Span y = span(Y, M * N, out_f32 ? 4 : 2);
+    if (M > 0 && (overlaps(y, span(X, M * K, 2)) || overlaps(y, span(gamma, K, 2)) ||
+                  overlaps(y, span(W, K * N, 2)) || (bias && overlaps(y, span(bias, N, 2)))))
+        return FUSE_E_ALIAS;
+    lf::Problem p{};
+    p.op = lf::Op::RmsGemm;
+    p.A = X;
+    p.W = W;
+    p.bias = bias;
+    p.gamma = gamma;
+    p.Y = Y;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.eps = eps;
+    p.act = act;
+    p.bf16 = bf16;
+    p.out_f32 = out_f32;
+    if (noalloc && lf::workspace_bytes(p) > lf::kScratchBytes) return FUSE_E_WORKSPACE;
+    return run(p, stream, noalloc);
 }
 
 }  // namespace
@@ -107,34 +143,13 @@ int fuse_gemm_epilogue(const void* A, const void* W, const void* bias, const voi
 int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps, const void* W,
                       const void* bias, void* Y, int64_t M, int64_t N, int64_t K, int act,
                       int dtype, void* stream) {
-    if (!gamma || !W || (M > 0 && (!X || !Y))) return FUSE_E_NULL;
-    bool bf16 = false, out_f32 = false;
-    if (int rc = check_dtype(dtype, &bf16, &out_f32)) return rc;
-    if (act < FUSE_ACT_NONE || act > FUSE_ACT_SILU) return FUSE_E_ENUM;
-    if (int rc = check_dims(M, N, K)) return rc;
-    if (int rc = check_eps(eps)) return rc;
-    if (!aligned16(X) || !aligned16(gamma) || !aligned16(W) || !aligned16(Y) ||
-        (bias && !aligned16(bias)))
-        return FUSE_E_ALIGN;
-    const Span y = span(Y, M * N, out_f32 ? 4 : 2);
-    if (M > 0 && (overlaps(y, span(X, M * K, 2)) || overlaps(y, span(gamma, K, 2)) ||
-                  overlaps(y, span(W, K * N, 2)) || (bias && overlaps(y, span(bias, N, 2)))))
-        return FUSE_E_ALIAS;
-    lf::Problem p{};
-    p.op = lf::Op::RmsGemm;
-    p.A = X;
-    p.W = W;
-    p.bias = bias;
-    p.gamma = gamma;
-    p.Y = Y;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.eps = eps;
-    p.act = act;
-    p.bf16 = bf16;
-    p.out_f32 = out_f32;
-    return run(p, stream);
+    return rmsnorm_gemm(X, gamma, eps, W, bias, Y, M, N, K, act, dtype, stream, false);
+}
+
+int fuse_rmsnorm_gemm_noalloc(const void* X, const void* gamma, float eps, const void* W,
+                              const void* bias, void* Y, int64_t M, int64_t N, int64_t K, int act,
+                              int dtype, void* stream) {
+    return rmsnorm_gemm(X, gamma, eps, W, bias, Y, M, N, K, act, dtype, stream, true);
 }
 
 int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps, const void* Wg,
@@ -206,6 +221,7 @@ const char* fuse_strerror(int status) {
     case FUSE_E_EPS: return "eps is negative or not finite";
     case FUSE_E_ALIAS: return "output overlaps an input";
     case FUSE_E_HIP: return "HIP runtime error at launch";
+    case FUSE_E_WORKSPACE: return "the call needs more split-K scratch than the fixed buffer holds";
     default: return "unknown status";
     }
 }

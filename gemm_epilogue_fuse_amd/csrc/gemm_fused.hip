@@ -209,6 +209,7 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 std::vector<void*> g_ws_retired;
 constexpr size_t kCounterBytes = 1 << 20;  // 256K tiles
 constexpr size_t kMinWorkspace = size_t(64) << 20;
+static_assert(kScratchBytes >= kCounterBytes, "scratch holds the arrival counters");
 
 __global__ void __launch_bounds__(256) zero_words_kernel(unsigned* p, int n) {
     const int i = blockIdx.x * 256 + threadIdx.x;
@@ -362,6 +363,53 @@ size_t split_bytes(const Plan& pl, const Problem& p, const KArgs& a) {
     return tiles * a.splits * per_split;
 }
 
+// Fixed split-K scratch for callers that cannot allocate: counters first,
+// partials after.  Each device holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it names
+// a stand-in, not device memory): its device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};
+
+// Device address of this device's scratch, its arrival counters zeroed on
+// `stream`.  The first call on a device looks the address up; until a zeroing
+// has run eagerly (and been waited for) on some stream of the device, every
+// call zeroes the counters on its own stream first, so a call captured into a
+// graph carries its own zeroing.
+hipError_t get_scratch(hipStream_t stream, float** ws, unsigned** cnt) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    unsigned char* base = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+    if (!g_scratch_zeroed[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return e;
+        e = zero_words(reinterpret_cast<unsigned*>(base), kCounterBytes, stream);
+        if (e != hipSuccess) return e;
+        if (cs == hipStreamCaptureStatusNone) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return e;
+            g_scratch_zeroed[dev] = true;
+        }
+    }
+    *cnt = reinterpret_cast<unsigned*>(base);
+    *ws = reinterpret_cast<float*>(base + kCounterBytes);
+    return hipSuccess;
+}
+
 }  // namespace
 
 size_t workspace_bytes(const Problem& p) {
@@ -372,7 +420,7 @@ size_t workspace_bytes(const Problem& p) {
     return kCounterBytes + split_bytes(*c.plan, p, a);
 }
 
-hipError_t launch(const Problem& p, hipStream_t stream) {
+hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
     if (p.M == 0) return hipSuccess;
     KArgs a;
     const Choice c = setup(p, a);
@@ -382,6 +430,12 @@ hipError_t launch(const Problem& p, hipStream_t stream) {
     const int nwg = a.tiles_m * a.tiles_n * a.splits;
     const void* fn = kernel_for((int)(c.plan - kPlans), p, a.splits > 1);
     if (fn == nullptr) return hipErrorInvalidDeviceFunction;
+    if (a.splits > 1 && noalloc) {
+        if (kCounterBytes + split_bytes(pl, p, a) > kScratchBytes) return hipErrorInvalidValue;
+        const hipError_t e = get_scratch(stream, &a.ws, &a.cnt);
+        if (e != hipSuccess) return e;
+        return launch_fn(fn, a, nwg, pl.threads(), stream);
+    }
     if (a.splits > 1) {
         std::lock_guard<std::mutex> lk(g_ws_mu);
         const hipError_t e = get_workspace(stream, split_bytes(pl, p, a), &a.ws, &a.cnt);

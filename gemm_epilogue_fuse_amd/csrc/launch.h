@@ -27,9 +27,15 @@ struct Problem {
     bool out_f32;   // output is float32
 };
 
+// Bytes of the fixed split-K scratch each device holds for calls that must
+// not allocate (1 MiB of arrival counters, then fp32 partials).
+constexpr size_t kScratchBytes = size_t(48) << 20;  // FUSE_NOALLOC_SCRATCH_BYTES
+
 // Enqueue the kernel(s) for `p` on `stream`.  Returns hipSuccess or the
-// launch error.
-hipError_t launch(const Problem& p, hipStream_t stream);
+// launch error.  With `noalloc`, a split-K plan exchanges its partials through
+// the fixed scratch instead of a per-stream workspace (no allocation; the
+// caller has checked that workspace_bytes(p) <= kScratchBytes).
+hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc = false);
 
 // Bytes of split-K workspace (partials and arrival counters) `launch` uses
 // for `p`; 0 when its plan does not split K.  No HIP call.

@@ -113,7 +113,9 @@ enum fuse_status {
     FUSE_E_ENUM = 4,  /* unknown act, dtype or flag                          */
     FUSE_E_EPS = 5,   /* eps < 0 or not finite                               */
     FUSE_E_ALIAS = 6, /* output overlaps an input (other than Y == residual) */
-    FUSE_E_HIP = 7    /* the HIP runtime reported an error at launch         */
+    FUSE_E_HIP = 7,   /* the HIP runtime reported an error at launch         */
+    FUSE_E_WORKSPACE = 8 /* fuse_rmsnorm_gemm_noalloc: the call needs more
+                            split-K scratch than FUSE_NOALLOC_SCRATCH_BYTES    */
 };
 
 /*
@@ -138,6 +140,28 @@ int fuse_gemm_epilogue(const void* A, const void* W, const void* bias,
 int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
                       const void* W, const void* bias, void* Y, int64_t M,
                       int64_t N, int64_t K, int act, int dtype, void* stream);
+
+/*
+ * fuse_rmsnorm_gemm for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks and results (bit for bit) as
+ * fuse_rmsnorm_gemm; it calls no hipMalloc, hipFree or allocating routine.
+ * A plan that splits K exchanges its partials through a fixed buffer of
+ * FUSE_NOALLOC_SCRATCH_BYTES that every device holds from its first such call
+ * until the process ends; a call whose plan needs more (fuse_workspace_bytes
+ * with op 1 tells beforehand; every automatic plan fits) returns
+ * FUSE_E_WORKSPACE before any HIP call.  Calls on one GPU share that buffer
+ * and its arrival counters whatever their stream, so calls that overlap in
+ * time on one GPU race and must be ordered by the caller (one stream, or
+ * events).  The first call on a device zeroes the counters on its stream and,
+ * outside capture, waits for that; a call captured before any eager call on
+ * its device captures the zeroing too.
+ */
+#define FUSE_NOALLOC_SCRATCH_BYTES (48u << 20)
+int fuse_rmsnorm_gemm_noalloc(const void* X, const void* gamma, float eps,
+                              const void* W, const void* bias, void* Y,
+                              int64_t M, int64_t N, int64_t K, int act,
+                              int dtype, void* stream);
 
 /*
  * H[M,F] = SiLU(Xhat . Wg) * (Xhat . Wu),  Xhat = RMSNorm_{gamma,eps}(X)

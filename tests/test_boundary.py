@@ -13,7 +13,7 @@ import gemm_epilogue_fuse_amd as lf
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fuse.h")
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_EPS, E_ALIAS, E_HIP = range(8)
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_EPS, E_ALIAS, E_HIP, E_WORKSPACE = range(9)
 
 # Fake, well-aligned device addresses far apart: validation never dereferences
 # them, and every call below fails validation (or is the M == 0 no-op), so no
@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.fuse_version() == 1
-    for code in range(8):
+    for code in range(9):
         s = L.fuse_strerror(code)
         assert s and s != b"unknown status"
     assert L.fuse_strerror(99) == b"unknown status"
@@ -247,5 +247,38 @@ def test_workspace_bytes_sizing(L):
     lf.set_plan("dma_128x128x64_s4:k16")
     try:
         assert lf.workspace_bytes(0, 4096, 4096, 8192) == MiB + 32 * 32 * 16 * (128 * 128 + 256 * 2) * 4
+    finally:
+        lf.set_plan(None)
+
+
+# --------------------------------------------------------------------------- allocation-free variant
+
+def rms_noalloc(L, X=A_, g=G_, eps=1e-6, W=W_, bias=None, Y=Y_, M=64, N=64, K=64, act=0, dtype=0):
+    return L.fuse_rmsnorm_gemm_noalloc(X, g, eps, W, bias, Y, M, N, K, act, dtype, None)
+
+
+def test_noalloc_checks_like_the_allocating_entry_point(L):
+    """Same argument checks, same statuses, before any HIP call."""
+    assert rms_noalloc(L, g=None) == E_NULL
+    assert rms_noalloc(L, M=4, N=12) == E_SHAPE
+    assert rms_noalloc(L, W=W_ + 8) == E_ALIGN
+    assert rms_noalloc(L, act=9) == E_ENUM
+    assert rms_noalloc(L, eps=-1.0) == E_EPS
+    assert rms_noalloc(L, Y=A_) == E_ALIAS
+    assert rms_noalloc(L, M=0, X=None, Y=None) == OK
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(L):
+    """A plan whose split-K partials exceed the fixed 48 MiB scratch is refused
+    with FUSE_E_WORKSPACE before any HIP call; every automatic plan fits."""
+    limit = 48 << 20
+    for M in (1, 32, 128, 512, 1024, 2048, 4096):
+        for N, K in ((1024, 1024), (4096, 4096), (4096, 11008), (11008, 4096), (2048, 8192)):
+            assert lf.workspace_bytes(1, M, N, K) <= limit, (M, N, K)
+    lf.set_plan("dma_128x128x64_s4:k16")
+    try:
+        assert lf.workspace_bytes(1, 1024, 4096, 8192) > limit
+        assert rms_noalloc(L, M=1024, N=4096, K=8192) == E_WORKSPACE
+        assert L.fuse_strerror(E_WORKSPACE) != b"unknown status"
     finally:
         lf.set_plan(None)
