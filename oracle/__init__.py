@@ -26,6 +26,13 @@ Parts and the passages they follow (page title, section):
 * ``rmsnorm_swiglu`` / ``swiglu_ffn`` -- "llm-fusion-compiler", FFN block
   (SwiGLU style: three GEMMs, activation, elementwise product, bias,
   residual).
+* ``layernorm`` / ``layernorm_gemm`` -- "llm-fusion-compiler", pattern table
+  (layernorm_gemm); the page names LayerNorm without printing it, so this is
+  the standard definition (mean, biased variance, eps inside the root, affine
+  gamma and beta).
+* ``prologue_bias_gemm`` -- deplodock post, Loop IR worked example
+  relu((x + bias) @ w): the bias is added to x inside the reduce, before the
+  products, and the activation follows the reduction.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
 that do not come from the oracle itself (identity and permutation weights,
@@ -81,6 +88,12 @@ def _load():
         lib.oracle_rmsnorm_gemm.argtypes = [dp, dp, ctypes.c_double, dp, dp, dp, i64, i64, i64, ctypes.c_int]
         lib.oracle_rmsnorm_swiglu.restype = ctypes.c_int
         lib.oracle_rmsnorm_swiglu.argtypes = [dp, dp, ctypes.c_double, dp, dp, dp, i64, i64, i64]
+        lib.oracle_layernorm.restype = None
+        lib.oracle_layernorm.argtypes = [dp, dp, dp, ctypes.c_double, dp, i64, i64]
+        lib.oracle_layernorm_gemm.restype = ctypes.c_int
+        lib.oracle_layernorm_gemm.argtypes = [dp, dp, dp, ctypes.c_double, dp, dp, dp, i64, i64, i64, ctypes.c_int]
+        lib.oracle_prologue_bias_gemm.restype = ctypes.c_int
+        lib.oracle_prologue_bias_gemm.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -179,3 +192,41 @@ def swiglu_ffn(X, gamma, eps, Wg, Wu, Wd, bias_d) -> np.ndarray:
     """Whole SwiGLU FFN block: Y = H @ Wd + bias_d + X, H from ``rmsnorm_swiglu``."""
     H = rmsnorm_swiglu(X, gamma, eps, Wg, Wu)
     return gemm_epilogue(H, Wd, bias_d, X, "none")
+
+
+def layernorm(X, gamma, eps, beta=None) -> np.ndarray:
+    """(X - mean) / sqrt(biased variance + eps) * gamma + beta over the last axis, in fp64."""
+    X, gamma, beta = _f64(X), _f64(gamma), _f64(beta)
+    M, K = X.shape
+    assert gamma.shape == (K,) and (beta is None or beta.shape == (K,))
+    out = np.empty_like(X)
+    _load().oracle_layernorm(_ptr(X), _ptr(gamma), _ptr(beta), float(eps), _ptr(out), M, K)
+    return out
+
+
+def layernorm_gemm(X, gamma, eps, W, beta=None, bias=None, act_kind="none") -> np.ndarray:
+    """Y = act(LayerNorm(X) @ W + bias) in fp64."""
+    X, gamma, beta, W, bias = _f64(X), _f64(gamma), _f64(beta), _f64(W), _f64(bias)
+    M, K = X.shape
+    K2, N = W.shape
+    assert K == K2 and gamma.shape == (K,)
+    Y = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_layernorm_gemm(_ptr(X), _ptr(gamma), _ptr(beta), float(eps), _ptr(W), _ptr(bias),
+                                       _ptr(Y), M, N, K, _act_code(act_kind))
+    if rc != 0:
+        raise ValueError("oracle_layernorm_gemm failed (%d)" % rc)
+    return Y
+
+
+def prologue_bias_gemm(A, abias, W, bias=None, residual=None, act_kind="none") -> np.ndarray:
+    """Y = act((A + abias) @ W + bias) + residual in fp64; abias [K] is added to every row of A."""
+    A, abias, W, bias, residual = _f64(A), _f64(abias), _f64(W), _f64(bias), _f64(residual)
+    M, K = A.shape
+    K2, N = W.shape
+    assert K == K2 and abias.shape == (K,)
+    Y = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_prologue_bias_gemm(_ptr(A), _ptr(abias), _ptr(W), _ptr(bias), _ptr(residual), _ptr(Y),
+                                           M, N, K, _act_code(act_kind))
+    if rc != 0:
+        raise ValueError("oracle_prologue_bias_gemm failed (%d)" % rc)
+    return Y

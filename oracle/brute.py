@@ -7,7 +7,10 @@ operand in either one shows up as a mismatch.
 
 Definitions followed (page title, section): "llm-fusion-compiler" pattern
 table (gemm -> bias -> activation, residual add after), deplodock post RMSNorm
-loop nest, "LLMBoost" section 3 (per-row rsqrt of mean square plus eps).
+loop nest, "LLMBoost" section 3 (per-row rsqrt of mean square plus eps),
+"llm-fusion-compiler" pattern table (layernorm_gemm: LayerNorm with mean,
+biased variance, eps inside the root, gamma and beta), deplodock post Loop IR
+example (relu((x + bias) @ w): bias added to x before the reduction).
 """
 from __future__ import annotations
 
@@ -73,3 +76,23 @@ def rmsnorm_swiglu(X, gamma, eps, Wg, Wu):
     G = matmul(xh, Wg)
     U = matmul(xh, Wu)
     return [[act(G[i][j], "silu") * U[i][j] for j in range(len(G[0]))] for i in range(len(G))]
+
+
+def layernorm(X, gamma, eps, beta=None):
+    out = []
+    for row in X:
+        n = len(row)
+        mu = sum(row) / n
+        var = sum((v - mu) * (v - mu) for v in row) / n
+        r = 1.0 / math.sqrt(var + eps)
+        out.append([(row[k] - mu) * r * gamma[k] + (beta[k] if beta is not None else 0.0) for k in range(n)])
+    return out
+
+
+def layernorm_gemm(X, gamma, eps, W, beta=None, bias=None, kind="none"):
+    return gemm_epilogue(layernorm(X, gamma, eps, beta), W, bias, None, kind)
+
+
+def prologue_bias_gemm(A, abias, W, bias=None, residual=None, kind="none"):
+    shifted = [[row[k] + abias[k] for k in range(len(row))] for row in A]
+    return gemm_epilogue(shifted, W, bias, residual, kind)

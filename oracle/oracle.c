@@ -24,6 +24,9 @@
  *    times x, times weight.
  *  - "LLMBoost" (saitejasrivilli), section 3 "CUDA Kernel":
  *    rsqrt(sum_sq / d_in + epsilon) per row.
+ *  - "llm-fusion-compiler", pattern table: layernorm_gemm (LayerNorm + GEMM);
+ *    deplodock post, Loop IR worked example: relu((x + bias) @ w), the bias
+ *    added to x inside the reduce (prologue) and relu applied after it.
  *
  * Loop order is i-k-j (row, reduction, column) purely so that the inner loop
  * walks contiguous memory; for each output element the k-sum still runs in
@@ -157,6 +160,59 @@ int oracle_rmsnorm_swiglu(const double* X, const double* gamma, double eps,
     for (int64_t i = 0; i < M * F; ++i) H[i] = silu(g[i]) * u[i];
     free(xh); free(g); free(u);
     return 0;
+}
+
+/* LayerNorm over the last axis ("llm-fusion-compiler" pattern table:
+ * layernorm_gemm; the page names the pattern without printing it, so this is
+ * the standard definition):
+ *   mu[m]  = (1/K) sum_k x[m,k]
+ *   var[m] = (1/K) sum_k (x[m,k] - mu[m])^2          (biased, centred)
+ *   out[m,k] = (x[m,k] - mu[m]) / sqrt(var[m] + eps) * gamma[k] + beta[k]
+ * beta may be NULL (zero).  eps sits inside the root, as for RMSNorm. */
+void oracle_layernorm(const double* X, const double* gamma, const double* beta,
+                      double eps, double* out, int64_t M, int64_t K) {
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        const double* x = X + m * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k) s += x[k];
+        const double mu = s / (double)K;
+        double v = 0.0;
+        for (int64_t k = 0; k < K; ++k) v += (x[k] - mu) * (x[k] - mu);
+        const double var = v / (double)K;
+        const double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t k = 0; k < K; ++k)
+            out[m * K + k] = (x[k] - mu) * rstd * gamma[k] + (beta ? beta[k] : 0.0);
+    }
+}
+
+/* Y = act( LayerNorm_{gamma,beta,eps}(X) . W + bias ) */
+int oracle_layernorm_gemm(const double* X, const double* gamma, const double* beta,
+                          double eps, const double* W, const double* bias,
+                          double* Y, int64_t M, int64_t N, int64_t K, int act) {
+    double* xh = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    if (!xh) return 2;
+    oracle_layernorm(X, gamma, beta, eps, xh, M, K);
+    int rc = oracle_gemm_epilogue(xh, W, bias, NULL, Y, M, N, K, act);
+    free(xh);
+    return rc;
+}
+
+/* Y = act( (A + abias) . W + bias ) + R: a bias on the GEMM's input, added to
+ * every row of A before the reduction (the deplodock post's Loop IR example
+ * relu((x + bias) @ w), where the add is the prologue inside the K loop),
+ * followed by the usual epilogue.  abias [K]; bias and R may be NULL. */
+int oracle_prologue_bias_gemm(const double* A, const double* abias, const double* W,
+                              const double* bias, const double* R, double* Y,
+                              int64_t M, int64_t N, int64_t K, int act) {
+    double* ab = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    if (!ab) return 2;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) ab[m * K + k] = A[m * K + k] + abias[k];
+    int rc = oracle_gemm_epilogue(ab, W, bias, R, Y, M, N, K, act);
+    free(ab);
+    return rc;
 }
 
 int oracle_abi_version(void) { return 1; }

@@ -334,3 +334,131 @@ def test_synth_is_seeded_and_ordered():
     assert not np.array_equal(a["X"], c["X"])
     gam = synth.widen(a["gamma"], synth.F16)
     assert abs(gam.mean() - 1.0) < 0.1 and 0.03 < gam.std() < 0.3
+
+
+# --------------------------------------------------------------------------
+# LayerNorm -> GEMM ("llm-fusion-compiler" pattern table: layernorm_gemm)
+# --------------------------------------------------------------------------
+
+def test_layernorm_matches_torch_layer_norm():
+    # torch.nn.functional.layer_norm in float64: mean, biased variance, eps
+    # inside the root, then gamma and beta (an unbiased variance or eps outside
+    # the root would differ by far more than 1e-12)
+    g = synth.generator(51)
+    for M, K in ((7, 40), (33, 257), (4, 4096)):
+        X = g.standard_normal((M, K)) * 3.0 + g.standard_normal((M, 1)) * 5.0
+        gamma = 1.0 + 0.1 * g.standard_normal(K)
+        beta = 0.1 * g.standard_normal(K)
+        for eps in (EPS32, 0.0, 1e-2):
+            ref = torch.nn.functional.layer_norm(torch.from_numpy(X), (K,), torch.from_numpy(gamma),
+                                                 torch.from_numpy(beta), eps).numpy()
+            assert np.allclose(oracle.layernorm(X, gamma, eps, beta), ref, rtol=1e-12, atol=1e-12)
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(X), (K,), torch.from_numpy(gamma), None, EPS32).numpy()
+        assert np.allclose(oracle.layernorm(X, gamma, EPS32), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layernorm_closed_form_moments():
+    # gamma = 1, beta = 0: every output row has mean 0 and variance
+    # var / (var + eps), i.e. exactly 1 with eps = 0
+    g = synth.generator(52)
+    X = g.standard_normal((9, 300)) * 2.0 + 7.0
+    for eps in (0.0, 0.5):
+        Y = oracle.layernorm(X, np.ones(300), eps)
+        var = X.var(axis=1)
+        assert np.allclose(Y.mean(axis=1), 0.0, atol=1e-13)
+        assert np.allclose(Y.var(axis=1), var / (var + eps), rtol=1e-12)
+
+
+def test_layernorm_shift_and_scale_invariance():
+    # LayerNorm(a x + c) == LayerNorm(x) for a > 0 and per-row constants c (eps = 0)
+    g = synth.generator(53)
+    X = g.standard_normal((6, 128))
+    gamma, beta = 1.0 + 0.1 * g.standard_normal(128), g.standard_normal(128)
+    base = oracle.layernorm(X, gamma, 0.0, beta)
+    moved = oracle.layernorm(4.0 * X + g.standard_normal((6, 1)) * 100.0, gamma, 0.0, beta)
+    assert np.allclose(moved, base, rtol=1e-10, atol=1e-10)
+
+
+def test_layernorm_of_zero_mean_rows_is_rmsnorm():
+    # rows built from +-v pairs have mean exactly 0, where LayerNorm (beta = 0)
+    # and RMSNorm share one definition; rmsnorm is pinned to torch separately
+    g = synth.generator(54)
+    half = g.standard_normal((5, 64))
+    X = np.concatenate([half, -half], axis=1)
+    gamma = 1.0 + 0.1 * g.standard_normal(128)
+    assert np.allclose(oracle.layernorm(X, gamma, EPS32), oracle.rmsnorm(X, gamma, EPS32), rtol=1e-13, atol=1e-15)
+
+
+def test_layernorm_gemm_identity_weight_and_numpy():
+    g = synth.generator(55)
+    X = g.standard_normal((12, 64)) + 3.0
+    gamma, beta = 1.0 + 0.1 * g.standard_normal(64), 0.1 * g.standard_normal(64)
+    xh = oracle.layernorm(X, gamma, EPS32, beta)
+    assert np.array_equal(oracle.layernorm_gemm(X, gamma, EPS32, np.eye(64), beta), xh)
+    W = g.standard_normal((64, 40)) / 8.0
+    b = 0.1 * g.standard_normal(40)
+    assert np.allclose(oracle.layernorm_gemm(X, gamma, EPS32, W, beta, b, "none"), xh @ W + b, rtol=1e-12,
+                       atol=1e-12)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (3, 7, 16), (16, 16, 64), (17, 9, 24)])
+@pytest.mark.parametrize("act_kind", ["none", "relu", "gelu_tanh", "silu"])
+def test_brute_force_layernorm_gemm(M, N, K, act_kind):
+    g = synth.generator(M * 100 + N * 10 + K)
+    X = g.standard_normal((M, K)) * 2.0 + 1.5
+    gamma, beta = 1.0 + 0.1 * g.standard_normal(K), 0.1 * g.standard_normal(K)
+    W = g.standard_normal((K, N)) / math.sqrt(K)
+    b = 0.1 * g.standard_normal(N)
+    want = brute.layernorm_gemm(X.tolist(), gamma.tolist(), EPS32, W.tolist(), beta.tolist(), b.tolist(), act_kind)
+    got = oracle.layernorm_gemm(X, gamma, EPS32, W, beta, b, act_kind)
+    assert np.allclose(got, np.array(want), rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Prologue bias: act((x + b) @ W + bias) + R (deplodock post, Loop IR example)
+# --------------------------------------------------------------------------
+
+def test_prologue_bias_worked_example_shape():
+    # the page's example relu((x + bias) @ w): x (16, 64), bias (64,), w (64, 16)
+    g = synth.generator(56)
+    x, ab, w = g.standard_normal((16, 64)), g.standard_normal(64), g.standard_normal((64, 16))
+    want = brute.prologue_bias_gemm(x.tolist(), ab.tolist(), w.tolist(), None, None, "relu")
+    got = oracle.prologue_bias_gemm(x, ab, w, act_kind="relu")
+    assert np.allclose(got, np.array(want), rtol=1e-12, atol=1e-12)
+    # and relu applies after the reduction, not to x + bias: numpy's matmul
+    assert np.allclose(got, np.maximum((x + ab) @ w, 0.0), rtol=1e-12, atol=1e-12)
+
+
+def test_prologue_bias_is_linear_in_the_bias():
+    # (A + 1 b) W = A W + 1 (b W): numpy matmul on both terms
+    g = synth.generator(57)
+    A, ab, W = g.standard_normal((20, 48)), g.standard_normal(48), g.standard_normal((48, 24))
+    bias, R = g.standard_normal(24), g.standard_normal((20, 24))
+    got = oracle.prologue_bias_gemm(A, ab, W, bias, R, "none")
+    assert np.allclose(got, A @ W + (ab @ W)[None, :] + bias + R, rtol=1e-12, atol=1e-12)
+
+
+def test_prologue_bias_identity_weight_and_integers():
+    g = synth.generator(58)
+    A = g.integers(-3, 4, (10, 32)).astype(np.float64)
+    ab = g.integers(-3, 4, 32).astype(np.float64)
+    # W = I: Y = act(A + b + bias) + R elementwise, exactly
+    bias = g.integers(-5, 6, 32).astype(np.float64)
+    R = g.integers(-5, 6, (10, 32)).astype(np.float64)
+    assert np.array_equal(oracle.prologue_bias_gemm(A, ab, np.eye(32), bias, R, "relu"),
+                          np.maximum(A + ab + bias, 0.0) + R)
+    # small integers: exact, equal to int64 matmul
+    W = g.integers(-2, 3, (32, 17))
+    want = (A.astype(np.int64) + ab.astype(np.int64)) @ W
+    assert np.array_equal(oracle.prologue_bias_gemm(A, ab, W.astype(np.float64)), want.astype(np.float64))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (5, 7, 16), (17, 9, 24)])
+@pytest.mark.parametrize("act_kind", ["none", "gelu_tanh", "silu"])
+def test_brute_force_prologue_bias(M, N, K, act_kind):
+    g = synth.generator(M * 97 + N * 13 + K)
+    A, ab, W = g.standard_normal((M, K)), g.standard_normal(K), g.standard_normal((K, N)) / math.sqrt(K)
+    b, R = 0.1 * g.standard_normal(N), g.standard_normal((M, N))
+    want = brute.prologue_bias_gemm(A.tolist(), ab.tolist(), W.tolist(), b.tolist(), R.tolist(), act_kind)
+    assert np.allclose(oracle.prologue_bias_gemm(A, ab, W, b, R, act_kind), np.array(want), rtol=1e-12,
+                       atol=1e-12)
