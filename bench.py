@@ -8,8 +8,9 @@ no bias, no activation ("LLMBoost", benchmark results: the [512,4096] x
 resident inputs.  ``workloads`` in the same line carries every other
 workload at its full size: the 64x256x256 GEMM + bias + GeLU, the GEMM +
 bias + activation sweep (M = 512..4096, N = K = 4096) with its SiLU, ReLU and
-residual variants, the bf16 SwiGLU FFN block (both kernels and their sum) and
-the decode-shaped RMSNorm -> Linear cells (B x D, fp16 and bf16).  Each
+residual variants, the bf16 SwiGLU FFN block (both kernels and their sum),
+LayerNorm -> Linear and the input-bias GEMM (the adjacent prologue fusions),
+and the decode-shaped RMSNorm -> Linear cells (B x D, fp16 and bf16).  Each
 carries its roofline fields and, beside it, the same computation unfused
 through torch (rms_norm, hipBLASLt matmul, separate elementwise kernels),
 timed the same way ("llm-fusion-compiler", benchmark table: generated kernel
@@ -317,6 +318,77 @@ def rms_workload(lf, name, M, D, N, dt, draw):
     return Workload(name, dt, 2.0 * M * N * D, alg, make, fused, unfused, lf.plan_name(1, M, N, D, code))
 
 
+def layernorm_workload(lf, name, M, D, N, act, dt):
+    """LayerNorm -> Linear + bias + activation (the layernorm_gemm pattern)."""
+    import torch
+    import torch.nn.functional as F
+    import numpy as np
+    import synth
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    alg = (M * D + 2 * D + D * N + N + M * N) * 2
+    code = _code(lf, dt)
+    L = lf.lib()
+    actc = lf.ACT[act]
+    eps = ctypes.c_float(1e-5)
+
+    def make():
+        g = synth.generator(0)
+        X = synth.normal(g, (M, D), 1.0)
+        fields = [("X", X), ("gamma", synth.normal(g, (D,), 0.1, 1.0)), ("beta", synth.normal(g, (D,), 0.1)),
+                  ("W", synth.normal(g, (D, N), 1.0 / np.sqrt(D))), ("bias", synth.normal(g, (N,), 0.1))]
+        base = {k: _dev(synth.to_bits(v, dt), dt) for k, v in fields}
+        return _sets(base, alg, lambda: {"Y": torch.empty((M, N), dtype=tdt, device="cuda:0")})
+
+    def fused(s):
+        args = (s["X"].data_ptr(), s["gamma"].data_ptr(), s["beta"].data_ptr(), eps, s["W"].data_ptr(),
+                s["bias"].data_ptr(), s["Y"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_layernorm_gemm(*args, M, N, D, actc, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_layernorm_gemm")
+        return call
+
+    def unfused(s):
+        X, g, be, W, b = s["X"], s["gamma"], s["beta"], s["W"], s["bias"]
+        return lambda st: F.gelu(torch.addmm(b, F.layer_norm(X, (D,), g, be, 1e-5), W), approximate="tanh")
+    return Workload(name, dt, 2.0 * M * N * D, alg, make, fused, unfused, lf.plan_name(3, M, N, D, code))
+
+
+def prologue_bias_workload(lf, name, M, K, N, act, dt):
+    """act((A + b) W + bias): the input bias added inside the reduction."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    alg = (M * K + K + K * N + N + M * N) * 2
+    code = _code(lf, dt)
+    L = lf.lib()
+    actc = lf.ACT[act]
+
+    def make():
+        g = synth.generator(0)
+        fields = [("A", synth.normal(g, (M, K), 1.0)), ("abias", synth.normal(g, (K,), 1.0)),
+                  ("W", synth.normal(g, (K, N), 1.0 / 64.0)), ("bias", synth.normal(g, (N,), 0.1))]
+        base = {k: _dev(synth.to_bits(v, dt), dt) for k, v in fields}
+        return _sets(base, alg, lambda: {"Y": torch.empty((M, N), dtype=tdt, device="cuda:0")})
+
+    def fused(s):
+        args = (s["A"].data_ptr(), s["abias"].data_ptr(), s["W"].data_ptr(), s["bias"].data_ptr(), None,
+                s["Y"].data_ptr())
+
+        def call(st):
+            rc = L.fuse_gemm_prologue_bias(*args, M, N, K, actc, code, ctypes.c_void_p(st.cuda_stream))
+            if rc:
+                raise lf.FuseError(rc, "fuse_gemm_prologue_bias")
+        return call
+
+    def unfused(s):
+        A, ab, W, b = s["A"], s["abias"], s["W"], s["bias"]
+        return lambda st: F.gelu(torch.addmm(b, A + ab, W), approximate="tanh")
+    return Workload(name, dt, 2.0 * M * N * K, alg, make, fused, unfused, lf.plan_name(4, M, N, K, code))
+
+
 def swiglu_workloads(lf, M, D, F_):
     """The bf16 SwiGLU FFN block as its two fused kernels, and their sum."""
     import torch
@@ -404,6 +476,11 @@ def all_workloads(lf):
         ws.append(gemm_workload(lf, name, M, 4096, 4096, act, resid, "f16",
                                 lambda M=M, resid=resid: synth.gemm_epilogue_sweep(M, seed=0, residual=resid)))
     ws += swiglu_workloads(lf, 2048, 4096, 11008)
+    # the adjacent prologue fusions: LayerNorm -> Linear and an input bias
+    ws.append(layernorm_workload(lf, "layernorm_gemm_gelu_tanh_2048x4096x4096_fp16", 2048, 4096, 4096,
+                                 "gelu_tanh", "f16"))
+    ws.append(prologue_bias_workload(lf, "prologue_bias_gemm_gelu_tanh_4096x4096x4096_fp16", 4096, 4096, 4096,
+                                     "gelu_tanh", "f16"))
     for dt in (synth.F16, synth.BF16):
         for D in (1024, 2048, 4096):
             for B in (1, 32, 128, 512, 1024):

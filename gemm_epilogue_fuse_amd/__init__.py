@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "gemm_epilogue", "rmsnorm_gemm", "rmsnorm_gemm_swiglu", "swiglu_ffn", "plan_name", "set_plan",
-    "workspace_bytes",
+    "workspace_bytes", "layernorm_gemm", "gemm_prologue_bias",
     "FuseError", "lib", "LIB_PATH", "ACT", "F16", "BF16", "OUT_F32",
 ]
 
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfuse.so"
 
 ACT = {"none": 0, "relu": 1, "gelu_tanh": 2, "silu": 3}
 F16, BF16, OUT_F32 = 0, 1, 0x100
-OP_GEMM, OP_RMS_GEMM, OP_RMS_SWIGLU = 0, 1, 2
+OP_GEMM, OP_RMS_GEMM, OP_RMS_SWIGLU, OP_LN_GEMM, OP_BIAS_GEMM = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.fuse_rmsnorm_gemm.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.fuse_rmsnorm_gemm_noalloc.restype = ci
         L.fuse_rmsnorm_gemm_noalloc.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.fuse_layernorm_gemm.restype = ci
+        L.fuse_layernorm_gemm.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.fuse_gemm_prologue_bias.restype = ci
+        L.fuse_gemm_prologue_bias.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.fuse_rmsnorm_gemm_swiglu.restype = ci
         L.fuse_rmsnorm_gemm_swiglu.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, i64, ci, vp]
         L.fuse_plan_name.restype = ctypes.c_char_p
@@ -178,6 +182,42 @@ def rmsnorm_gemm(X, gamma, W, eps=1e-6, bias=None, act="none", out=None, out_dty
             _stream(X.device))
     if rc != 0:
         raise FuseError(rc, "fuse_rmsnorm_gemm_noalloc" if noalloc else "fuse_rmsnorm_gemm")
+    return Y
+
+
+def layernorm_gemm(X, gamma, W, eps=1e-5, beta=None, bias=None, act="none", out=None, out_dtype=None):
+    """Y = act(LayerNorm_{gamma,beta,eps}(X) @ W + bias); the normalised X stays on chip."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[1]
+    _check(gamma, "gamma", X.dtype, (K,), X.device)
+    _check(beta, "beta", X.dtype, (K,), X.device)
+    _check(W, "W", X.dtype, (K, N), X.device)
+    _check(bias, "bias", X.dtype, (N,), X.device)
+    code = _dtype_code(X, out_dtype)
+    Y = _out(out, (M, N), torch.float32 if code & OUT_F32 else X.dtype, X.device)
+    rc = lib().fuse_layernorm_gemm(_ptr(X), _ptr(gamma), _ptr(beta), float(eps), _ptr(W), _ptr(bias), _ptr(Y),
+                                   M, N, K, _act(act), code, _stream(X.device))
+    if rc != 0:
+        raise FuseError(rc, "fuse_layernorm_gemm")
+    return Y
+
+
+def gemm_prologue_bias(A, abias, W, bias=None, residual=None, act="none", out=None, out_dtype=None):
+    """Y = act((A + abias) @ W + bias) + residual; abias [K] is added to A inside the reduction."""
+    torch = _torch()
+    M, K = A.shape
+    N = W.shape[1]
+    _check(abias, "abias", A.dtype, (K,), A.device)
+    _check(W, "W", A.dtype, (K, N), A.device)
+    _check(bias, "bias", A.dtype, (N,), A.device)
+    _check(residual, "residual", A.dtype, (M, N), A.device)
+    code = _dtype_code(A, out_dtype)
+    Y = _out(out, (M, N), torch.float32 if code & OUT_F32 else A.dtype, A.device)
+    rc = lib().fuse_gemm_prologue_bias(_ptr(A), _ptr(abias), _ptr(W), _ptr(bias), _ptr(residual), _ptr(Y),
+                                       M, N, K, _act(act), code, _stream(A.device))
+    if rc != 0:
+        raise FuseError(rc, "fuse_gemm_prologue_bias")
     return Y
 
 

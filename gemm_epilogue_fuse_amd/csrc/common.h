@@ -24,7 +24,9 @@ struct KArgs {
     const uint16_t* W2;
     const uint16_t* bias;
     const uint16_t* resid;
-    const uint16_t* gamma;
+    const uint16_t* gamma;  // [K]: RMSNorm/LayerNorm gamma, or the input bias of the prologue-bias GEMM
+    const uint16_t* beta;   // [K] LayerNorm beta (nullptr: zero)
+    const float2* stats;    // [M] LayerNorm row statistics (a, b): the operand is a*x + b before gamma, beta
     void* Y;
     int M, N, K;
     int tiles_m, tiles_n, group_m;
@@ -159,7 +161,7 @@ __device__ __forceinline__ float apply_act(float z) {
 // therefore checks its rows after the reduction -- mean square plus eps inside
 // [lo, hi] and every accumulator finite (an operand that overflowed leaves an
 // inf or NaN in every column of its row) -- and if any row fails, recomputes
-// its whole tile with rms_exact_tile: r in fp64, the normalised activation
+// its whole tile with prologue_exact_tile: r in fp64, the normalised activation
 // x * r * gamma (deplodock post, RMSNorm loop nest; "LLMBoost", section 3) as
 // an fp32 operand, products accumulated in fp32.  Inside the window the fast
 // path's operand error stays at or below the rounding of the normalised value
@@ -175,20 +177,33 @@ __device__ __forceinline__ bool rms_outside(float ss, int K, float eps) {
     return !(ms + eps >= (BF ? kRmsLoBF16 : kRmsLoF16)) || !(ms <= kRmsHi);
 }
 
-// Recompute output rows [m0, m0 + BM) x columns [n0, n0 + BN) of an RMS call
-// (NB = 2: the SwiGLU gate/up pair, H = SiLU(g) * u) from global memory with
-// plain arithmetic.  Every thread of the NT-thread workgroup calls it; `lds`
-// needs 16 * 8 + 16 * 64 * 4 bytes.  Slow (no matrix cores, no staging of W),
-// and only reached by tiles holding rows outside the fast path's window.
-template <bool BF, int NB, int NT, int BN>
-__device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0, int BM, int n0) {
+// Prologue of the A operand, applied elementwise on the way to the matrix
+// cores: none, RMSNorm (x * gamma, row factor applied after the reduction),
+// input bias (x + b), LayerNorm (per-row a*x + b from precomputed statistics,
+// then * gamma + beta).
+enum Prologue : int { kProNone = 0, kProRms = 1, kProBias = 2, kProLn = 3 };
+
+// Recompute output rows [m0, m0 + BM) x columns [n0, n0 + BN) with plain
+// arithmetic from global memory: the exact path of the prologue PRO (RMS
+// calls: also NB = 2, the SwiGLU gate/up pair, H = SiLU(g) * u).  The
+// operand is the method's value in fp32, never rounded to the input type:
+//   RMS   x * r * gamma,            r = 1 / sqrt(mean(x^2) + eps) in fp64
+//   bias  x + b
+//   LN    (x - mu) * rstd * gamma + beta, mu and rstd = 1/sqrt(var + eps) in fp64
+// and products are accumulated in fp32; bias, activation and residual follow.
+// Every thread of the NT-thread workgroup calls it; `lds` needs
+// 16 * 16 + 16 * 64 * 4 bytes.  Slow (no matrix cores, no staging of W), and
+// only reached by tiles whose fast path left its range.
+template <bool BF, int NB, int NT, int BN, int PRO = kProRms>
+__device__ __forceinline__ void prologue_exact_tile(const KArgs& p, char* lds, int m0, int BM, int n0) {
     constexpr int RC = 16, KC = 64, NW = NT / 64;
     static_assert(NT % BN == 0, "whole threads per output column");
     constexpr int TPC = NT / BN;               // threads per output column
     static_assert(TPC >= RC || RC % TPC == 0, "rows of a chunk split evenly");
     constexpr int RPT = (RC + TPC - 1) / TPC;  // rows of a chunk per thread
-    double* rr = reinterpret_cast<double*>(lds);
-    float* op = reinterpret_cast<float*>(lds + RC * sizeof(double));
+    double* rr = reinterpret_cast<double*>(lds);       // RMS r, LN rstd
+    double* mu = rr + RC;                              // LN mean
+    float* op = reinterpret_cast<float*>(lds + 2 * RC * sizeof(double));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int N = p.N, K = p.K;
     const int rows = min(BM, p.M - m0);
@@ -197,16 +212,27 @@ __device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0
     __syncthreads();  // the caller's LDS use is over
     for (int r0 = 0; r0 < rows; r0 += RC) {
         const int rc = min(RC, rows - r0);
-        // r = 1 / sqrt(mean_k x^2 + eps) in fp64, one wave per row
-        for (int i = wave; i < rc; i += NW) {
-            const uint16_t* x = p.A + (size_t)(m0 + r0 + i) * K;
-            double s = 0.0;
-            for (int k = lane; k < K; k += 64) {
-                const double v = (double)h_f32<BF>(x[k]);
-                s = fma(v, v, s);
+        // per-row factors in fp64, one wave per row
+        if constexpr (PRO == kProRms || PRO == kProLn) {
+            for (int i = wave; i < rc; i += NW) {
+                const uint16_t* x = p.A + (size_t)(m0 + r0 + i) * K;
+                double m = 0.0;
+                if constexpr (PRO == kProLn) {
+                    for (int k = lane; k < K; k += 64) m += (double)h_f32<BF>(x[k]);
+                    for (int o = 32; o > 0; o >>= 1) m += __shfl_xor(m, o);
+                    m /= (double)K;
+                }
+                double s = 0.0;
+                for (int k = lane; k < K; k += 64) {
+                    const double v = (double)h_f32<BF>(x[k]) - m;
+                    s = fma(v, v, s);
+                }
+                for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+                if (lane == 0) {
+                    rr[i] = 1.0 / sqrt(s / (double)K + (double)p.eps);
+                    mu[i] = m;
+                }
             }
-            for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-            if (lane == 0) rr[i] = 1.0 / sqrt(s / (double)K + (double)p.eps);
         }
         float acc[NB][RPT];
 #pragma unroll
@@ -218,9 +244,15 @@ __device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0
             for (int e = tid; e < RC * KC; e += NT) {
                 const int i = e / KC, k = k0 + e % KC;
                 float v = 0.0f;
-                if (i < rc && k < K)
-                    v = (float)((double)h_f32<BF>(p.A[(size_t)(m0 + r0 + i) * K + k]) * rr[i] *
-                                (double)h_f32<BF>(p.gamma[k]));
+                if (i < rc && k < K) {
+                    const double x = (double)h_f32<BF>(p.A[(size_t)(m0 + r0 + i) * K + k]);
+                    const double g = (double)h_f32<BF>(p.gamma[k]);
+                    if constexpr (PRO == kProRms) v = (float)(x * rr[i] * g);
+                    else if constexpr (PRO == kProBias) v = (float)(x + g);
+                    else if constexpr (PRO == kProLn)
+                        v = (float)((x - mu[i]) * rr[i] * g + (p.beta ? (double)h_f32<BF>(p.beta[k]) : 0.0));
+                    else v = (float)x;
+                }
                 op[e] = v;
             }
             __syncthreads();
@@ -245,6 +277,7 @@ __device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0
             for (int j = 0; j < RPT; ++j) {
                 const int i = rsub + j * TPC;
                 if (i >= rc) continue;
+                const size_t o = (size_t)(m0 + r0 + i) * N + n0 + c;
                 float z;
                 if constexpr (NB == 2) {
                     z = silu(acc[0][j]) * acc[NB - 1][j];
@@ -256,8 +289,8 @@ __device__ __forceinline__ void rms_exact_tile(const KArgs& p, char* lds, int m0
                     case 3: z = apply_act<3>(z); break;
                     default: break;
                     }
+                    if (p.resid != nullptr) z += h_f32<BF>(p.resid[o]);
                 }
-                const size_t o = (size_t)(m0 + r0 + i) * N + n0 + c;
                 if (p.out_f32) static_cast<float*>(p.Y)[o] = z;
                 else static_cast<uint16_t*>(p.Y)[o] = f32_h<BF>(z);
             }

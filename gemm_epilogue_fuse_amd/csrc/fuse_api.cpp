@@ -1,5 +1,5 @@
 // fuse_api.cpp -- the C ABI declared in include/fuse.h: argument checks, then
-// one kernel launch on the caller's stream.
+// the kernel launch(es) on the caller's stream.
 //
 // Checks mirror the shape verifier that the "LLMBoost" fused op runs before
 // execution (section 1): every argument is validated on the host, with no
@@ -183,8 +183,79 @@ int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps, const 
     return run(p, stream);
 }
 
+int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta, float eps, const void* W,
+                        const void* bias, void* Y, int64_t M, int64_t N, int64_t K, int act, int dtype,
+                        void* stream) {
+    if (!gamma || !W || (M > 0 && (!X || !Y))) return FUSE_E_NULL;
+    bool bf16 = false, out_f32 = false;
+    if (int rc = check_dtype(dtype, &bf16, &out_f32)) return rc;
+    if (act < FUSE_ACT_NONE || act > FUSE_ACT_SILU) return FUSE_E_ENUM;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (int rc = check_eps(eps)) return rc;
+    if (!aligned16(X) || !aligned16(gamma) || (beta && !aligned16(beta)) || !aligned16(W) || !aligned16(Y) ||
+        (bias && !aligned16(bias)))
+        return FUSE_E_ALIGN;
+    const Span y = span(Y, M * N, out_f32 ? 4 : 2);
+    if (M > 0 && (overlaps(y, span(X, M * K, 2)) || overlaps(y, span(gamma, K, 2)) ||
+                  (beta && overlaps(y, span(beta, K, 2))) || overlaps(y, span(W, K * N, 2)) ||
+                  (bias && overlaps(y, span(bias, N, 2)))))
+        return FUSE_E_ALIAS;
+    lf::Problem p{};
+    p.op = lf::Op::LnGemm;
+    p.A = X;
+    p.W = W;
+    p.bias = bias;
+    p.gamma = gamma;
+    p.beta = beta;
+    p.Y = Y;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.eps = eps;
+    p.act = act;
+    p.bf16 = bf16;
+    p.out_f32 = out_f32;
+    return run(p, stream);
+}
+
+int fuse_gemm_prologue_bias(const void* A, const void* abias, const void* W, const void* bias,
+                            const void* residual, void* Y, int64_t M, int64_t N, int64_t K, int act, int dtype,
+                            void* stream) {
+    if (!abias || !W || (M > 0 && (!A || !Y))) return FUSE_E_NULL;
+    bool bf16 = false, out_f32 = false;
+    if (int rc = check_dtype(dtype, &bf16, &out_f32)) return rc;
+    if (act < FUSE_ACT_NONE || act > FUSE_ACT_SILU) return FUSE_E_ENUM;
+    if (int rc = check_dims(M, N, K)) return rc;
+    if (!aligned16(A) || !aligned16(abias) || !aligned16(W) || !aligned16(Y) || (bias && !aligned16(bias)) ||
+        (residual && !aligned16(residual)))
+        return FUSE_E_ALIGN;
+    const Span y = span(Y, M * N, out_f32 ? 4 : 2);
+    if (M > 0) {
+        if (overlaps(y, span(A, M * K, 2)) || overlaps(y, span(abias, K, 2)) || overlaps(y, span(W, K * N, 2)) ||
+            (bias && overlaps(y, span(bias, N, 2))))
+            return FUSE_E_ALIAS;
+        if (residual && overlaps(y, span(residual, M * N, 2)) && !(residual == Y && !out_f32))
+            return FUSE_E_ALIAS;
+    }
+    lf::Problem p{};
+    p.op = lf::Op::BiasGemm;
+    p.A = A;
+    p.gamma = abias;
+    p.W = W;
+    p.bias = bias;
+    p.resid = residual;
+    p.Y = Y;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.act = act;
+    p.bf16 = bf16;
+    p.out_f32 = out_f32;
+    return run(p, stream);
+}
+
 const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype) {
-    if (op < 0 || op > 2) return "invalid";
+    if (op < 0 || op > 4) return "invalid";
     lf::Problem p{};
     p.op = static_cast<lf::Op>(op);
     p.M = M;
@@ -196,7 +267,7 @@ const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype) {
 }
 
 int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype) {
-    if (op < 0 || op > 2) return -1;
+    if (op < 0 || op > 4) return -1;
     bool bf16 = false, out_f32 = false;
     if (check_dtype(dtype, &bf16, &out_f32) != FUSE_OK || check_dims(M, N, K) != FUSE_OK) return -1;
     lf::Problem p{};

@@ -84,8 +84,12 @@ std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
 std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
 
 
+// The LayerNorm and input-bias prologues exist in the register-staged kernel only.
+bool reg_only(const Problem& p) { return p.op == Op::LnGemm || p.op == Op::BiasGemm; }
+
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
+    if (reg_only(p) && pl.kind != Kind::Reg) return false;
     if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
     if (pl.kind == Kind::Strip && p.op != Op::GemmEpilogue && p.K > dev::kStripMaxK) return false;
     if (pl.kind == Kind::WStrip && p.K > dev::kWStripMaxK) return false;
@@ -145,6 +149,10 @@ Choice choose(const Problem& p) {
         return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
     }
     const Plan* pl;
+    if (reg_only(p)) {
+        const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+        return {(t256 >= 224) ? &kPlans[kReg256] : &kPlans[kReg128], 1};
+    }
     if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
         // a few rows and a short K: one workgroup per 16-column strip over
         // all of K (no partial sums cross the device), the whole strip in
@@ -223,6 +231,42 @@ hipError_t zero_words(unsigned* p, size_t bytes, hipStream_t stream) {
                            args, 0, stream);
 }
 
+// LayerNorm row statistics ("llm-fusion-compiler" pattern table:
+// layernorm_gemm, the statistics pass of a two-kernel LayerNorm + GEMM): one
+// wave per row, mean and centred variance in fp64 over two passes of the row,
+// stored as the fp32 pair (a, b) = (1/sqrt(var + eps), -mean * a), so that the
+// GEMM's prologue forms (a*x + b) * gamma + beta.  Rows are 16-byte aligned
+// (K % 8 == 0), so each lane reads 8 values at a time.
+template <bool BF>
+__global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M, int K, float eps, float2* out) {
+    const int lane = threadIdx.x & 63;
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const uint16_t* x = X + (size_t)m * K;
+    double s = 0.0;
+    for (int k = 8 * lane; k < K; k += 512) {
+        const dev::u32x4 v = *reinterpret_cast<const dev::u32x4*>(x + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s += (double)dev::lo_f32<BF>(v[q]) + (double)dev::hi_f32<BF>(v[q]);
+    }
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    const double mu = s / (double)K;
+    double v2 = 0.0;
+    for (int k = 8 * lane; k < K; k += 512) {
+        const dev::u32x4 v = *reinterpret_cast<const dev::u32x4*>(x + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double d0 = (double)dev::lo_f32<BF>(v[q]) - mu, d1 = (double)dev::hi_f32<BF>(v[q]) - mu;
+            v2 = fma(d0, d0, fma(d1, d1, v2));
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) v2 += __shfl_xor(v2, o);
+    if (lane == 0) {
+        const double a = 1.0 / sqrt(v2 / (double)K + (double)eps);
+        out[m] = make_float2((float)a, (float)(-mu * a));
+    }
+}
+
 // Caller holds g_ws_mu.
 hipError_t get_workspace(hipStream_t stream, size_t part_bytes, float** ws, unsigned** cnt) {
     int dev = 0;
@@ -263,8 +307,19 @@ hipError_t launch_fn(const void* fn, const KArgs& a, int nwg, int threads, hipSt
 }
 
 // The kernel of plan `pi` for this call, from the unit that instantiates it.
+int prologue_of(const Problem& p) {
+    switch (p.op) {
+    case Op::RmsGemm:
+    case Op::RmsSwiglu: return dev::kProRms;
+    case Op::BiasGemm: return dev::kProBias;
+    case Op::LnGemm: return dev::kProLn;
+    default: return dev::kProNone;
+    }
+}
+
 const void* kernel_for(int pi, const Problem& p, bool split) {
-    const KernelSel s{pi, p.bf16, p.op != Op::GemmEpilogue, split, (int)p.K};
+    const int pro = prologue_of(p);
+    const KernelSel s{pi, p.bf16, pro == dev::kProRms, pro, split, (int)p.K};
     switch (kPlans[pi].kind) {
     case Kind::Reg: return kernels_reg(s);
     case Kind::Dec:
@@ -326,6 +381,8 @@ Choice setup(const Problem& p, KArgs& a) {
     a.bias = static_cast<const uint16_t*>(p.bias);
     a.resid = static_cast<const uint16_t*>(p.resid);
     a.gamma = static_cast<const uint16_t*>(p.gamma);
+    a.beta = static_cast<const uint16_t*>(p.beta);
+    a.stats = nullptr;
     a.Y = p.Y;
     a.M = (int)p.M;
     a.N = (int)p.N;
@@ -412,12 +469,15 @@ hipError_t get_scratch(hipStream_t stream, float** ws, unsigned** cnt) {
 
 }  // namespace
 
+// Bytes of LayerNorm row statistics a call keeps in the workspace.
+size_t stats_bytes(const Problem& p) { return p.op == Op::LnGemm ? (size_t)p.M * sizeof(float2) : 0; }
+
 size_t workspace_bytes(const Problem& p) {
     if (p.M == 0) return 0;
     KArgs a;
     const Choice c = setup(p, a);
-    if (a.splits == 1) return 0;
-    return kCounterBytes + split_bytes(*c.plan, p, a);
+    if (a.splits == 1 && stats_bytes(p) == 0) return 0;
+    return kCounterBytes + (a.splits > 1 ? split_bytes(*c.plan, p, a) : 0) + stats_bytes(p);
 }
 
 hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
@@ -433,6 +493,26 @@ hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
     if (a.splits > 1 && noalloc) {
         if (kCounterBytes + split_bytes(pl, p, a) > kScratchBytes) return hipErrorInvalidValue;
         const hipError_t e = get_scratch(stream, &a.ws, &a.cnt);
+        if (e != hipSuccess) return e;
+        return launch_fn(fn, a, nwg, pl.threads(), stream);
+    }
+    if (p.op == Op::LnGemm) {
+        // two kernels: the row statistics into the workspace, then the GEMM
+        // whose prologue normalises each A element on its way to LDS
+        std::lock_guard<std::mutex> lk(g_ws_mu);
+        float* ws = nullptr;
+        unsigned* cnt = nullptr;
+        hipError_t e = get_workspace(stream, stats_bytes(p), &ws, &cnt);
+        if (e != hipSuccess) return e;
+        a.stats = reinterpret_cast<const float2*>(ws);
+        const uint16_t* X = a.A;
+        int M = a.M, K = a.K;
+        float eps = a.eps;
+        float2* out = reinterpret_cast<float2*>(ws);
+        void* sargs[] = {&X, &M, &K, &eps, &out};
+        const void* sfn = p.bf16 ? reinterpret_cast<const void*>(&ln_stats_kernel<true>)
+                                 : reinterpret_cast<const void*>(&ln_stats_kernel<false>);
+        e = hipLaunchKernel(sfn, dim3((M + 3) / 4), dim3(256), sargs, 0, stream);
         if (e != hipSuccess) return e;
         return launch_fn(fn, a, nwg, pl.threads(), stream);
     }

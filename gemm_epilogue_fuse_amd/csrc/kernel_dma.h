@@ -755,7 +755,7 @@ gemm_dma_kernel(const KArgs p) {
         bad |= !__builtin_isfinite(t);
         __syncthreads();
         if (__syncthreads_or(bad)) {
-            rms_exact_tile<BF, NB, NT, BN>(p, smem, m0, BM, n0);
+            prologue_exact_tile<BF, NB, NT, BN>(p, smem, m0, BM, n0);
             return;
         }
     }

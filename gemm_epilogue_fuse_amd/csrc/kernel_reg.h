@@ -10,8 +10,11 @@
 //     XOR-swizzled by the row, so fragment reads and tile writes avoid bank
 //     conflicts;
 //   * two LDS stages and one or two register sets of lookahead;
-//   * v_mfma_f32_32x32x16_{f16,bf16}; RMS prologue folded into the staging
-//     (X scaled by gamma, sum of squares from the same registers).
+//   * v_mfma_f32_32x32x16_{f16,bf16}; the A prologue folded into the staging,
+//     once per element and workgroup: RMSNorm (X scaled by gamma, sum of
+//     squares from the same registers), an input bias (x + b), or LayerNorm
+//     (a*x + b from the row statistics, then * gamma + beta), each computed
+//     in fp32 and rounded once to the input type.
 // Handles any K that is a multiple of 8 (the KT variant masks the K tail).
 #pragma once
 
@@ -25,9 +28,10 @@ constexpr int kKCH = kBK / 8;    // 16-byte chunks per LDS row
 
 // ---------------------------------------------------------------- kernel
 
-template <int BM, int BN, int WM, int WN, bool BF, bool RMS, int NB, int NREG, bool KT>
+template <int BM, int BN, int WM, int WN, bool BF, int PRO, int NB, int NREG, bool KT>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_fused_kernel(const KArgs p) {
+    constexpr bool RMS = PRO == kProRms;
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
@@ -64,7 +68,9 @@ gemm_fused_kernel(const KArgs p) {
     const uint32_t w_bytes = (uint32_t)(((size_t)K * N - n0) * 2);
     const auto rsW = make_rsrc(p.W + n0, w_bytes);
     const auto rsW2 = make_rsrc(NB == 2 ? p.W2 + n0 : p.W + n0, w_bytes);
-    const auto rsG = make_rsrc(p.gamma, RMS ? (uint32_t)K * 2 : 0u);
+    const auto rsG = make_rsrc(p.gamma, PRO != kProNone ? (uint32_t)K * 2 : 0u);
+    // LayerNorm beta; absent, its loads read zeros
+    const auto rsBe = make_rsrc(p.beta ? p.beta : p.A, (PRO == kProLn && p.beta) ? (uint32_t)K * 2 : 0u);
 
     // Thread -> A chunk mapping: row a_row0 + i*A_ROW_STEP, chunk a_kc.
     const int a_kc = tid % kKCH;
@@ -75,13 +81,22 @@ gemm_fused_kernel(const KArgs p) {
     struct Regs {
         u32x4 a[A_PER];
         u32x4 b[B_PER][KB];
-        u32x4 g;
+        u32x4 g;   // gamma, or the input bias
+        u32x4 be;  // LayerNorm beta
     };
     Regs R0;
     Regs R1;  // unused when NREG == 1
     float ss[A_PER];
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) ss[i] = 0.0f;
+    // LayerNorm: the operand of row m is (a[m] x + b[m]) * gamma + beta
+    float2 lnab[A_PER];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+        const int row = m0 + a_row0 + i * A_ROW_STEP;
+        lnab[i] = make_float2(0.0f, 0.0f);
+        if (PRO == kProLn && row < M) lnab[i] = p.stats[row];
+    }
 
     f32x16 acc[NB][FM][FN];
 #pragma unroll
@@ -123,7 +138,8 @@ gemm_fused_kernel(const KArgs p) {
         const bool kaok = !KT || (k0 + a_kc * 8 < K);
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) R.a[i] = bload16(rsA, KT ? oob_or(offA[i], kaok) : offA[i], sA);
-        if constexpr (RMS) R.g = bload16(rsG, oob_or((uint32_t)a_kc * 16u, k0 + a_kc * 8 < K), sA);
+        if constexpr (PRO != kProNone) R.g = bload16(rsG, oob_or((uint32_t)a_kc * 16u, k0 + a_kc * 8 < K), sA);
+        if constexpr (PRO == kProLn) R.be = bload16(rsBe, oob_or((uint32_t)a_kc * 16u, k0 + a_kc * 8 < K), sA);
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
             const auto rs = (NB == 2 && opnd_of[i] == 1) ? rsW2 : rsW;
@@ -150,6 +166,22 @@ gemm_fused_kernel(const KArgs p) {
                     ss[i] = fmaf(x0, x0, ss[i]);
                     ss[i] = fmaf(x1, x1, ss[i]);
                     o[q] = pack2<BF>(x0 * lo_f32<BF>(R.g[q]), x1 * hi_f32<BF>(R.g[q]));
+                }
+                v = o;
+            } else if constexpr (PRO == kProBias) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    o[q] = pack2<BF>(lo_f32<BF>(v[q]) + lo_f32<BF>(R.g[q]), hi_f32<BF>(v[q]) + hi_f32<BF>(R.g[q]));
+                v = o;
+            } else if constexpr (PRO == kProLn) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float t0 = fmaf(lo_f32<BF>(v[q]), lnab[i].x, lnab[i].y);
+                    const float t1 = fmaf(hi_f32<BF>(v[q]), lnab[i].x, lnab[i].y);
+                    o[q] = pack2<BF>(fmaf(t0, lo_f32<BF>(R.g[q]), lo_f32<BF>(R.be[q])),
+                                     fmaf(t1, hi_f32<BF>(R.g[q]), hi_f32<BF>(R.be[q])));
                 }
                 v = o;
             }
@@ -280,7 +312,24 @@ gemm_fused_kernel(const KArgs p) {
         bad |= !__builtin_isfinite(t);
         __syncthreads();
         if (__syncthreads_or(bad)) {
-            rms_exact_tile<BF, NB, NT, BN>(p, reinterpret_cast<char*>(lds), m0, BM, n0);
+            prologue_exact_tile<BF, NB, NT, BN>(p, reinterpret_cast<char*>(lds), m0, BM, n0);
+            return;
+        }
+    } else if constexpr (PRO == kProBias || PRO == kProLn) {
+        // an operand that left the input type's range (x + b, or a normalised
+        // value past the fp16 maximum) leaves a non-finite accumulator:
+        // recompute the tile with fp32 operands
+        float t = 0.0f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) t += acc[b][i][j][r];
+        if (__syncthreads_or(!__builtin_isfinite(t))) {
+            prologue_exact_tile<BF, NB, NT, BN, PRO>(p, reinterpret_cast<char*>(lds), m0, BM, n0);
             return;
         }
     }

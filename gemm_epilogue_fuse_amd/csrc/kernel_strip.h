@@ -197,7 +197,7 @@ gemm_strip_kernel(const KArgs p) {
             bad = rms_outside<BF>(s, K, p.eps) || !__builtin_isfinite(t);
         }
         if (__syncthreads_or(bad)) {
-            rms_exact_tile<BF, 1, NT, BN>(p, smem, m0, BM, n0);
+            prologue_exact_tile<BF, 1, NT, BN>(p, smem, m0, BM, n0);
             return;
         }
     }

@@ -189,7 +189,7 @@ gemm_wstrip_kernel(const KArgs p) {
             bad = rms_outside<BF>(s, K, p.eps) || !__builtin_isfinite(t);
         }
         if (__syncthreads_or(bad)) {
-            rms_exact_tile<BF, 1, NW * 64, BN>(p, smem, m0, BM, n0);
+            prologue_exact_tile<BF, 1, NW * 64, BN>(p, smem, m0, BM, n0);
             return;
         }
     }

@@ -33,6 +33,7 @@ struct KernelSel {
     int plan;    // PlanIndex
     bool bf16;   // bf16 inputs (else fp16)
     bool rms;    // RMSNorm prologue (RmsGemm, RmsSwiglu)
+    int pro;     // A prologue: 0 none, 1 RMSNorm, 2 input bias, 3 LayerNorm (dev::Prologue)
     bool split;  // split-K partial exchange compiled in
     int K;       // reduction length (the register-staged kernel has a K-tail variant)
 };
@@ -41,7 +42,7 @@ struct KernelSel {
 // holds no kernel for `s`.
 const void* kernels_dma_square(const KernelSel& s);  // k_dma_square.hip: 128x128 and 256x256 tiles
 const void* kernels_dma_wide(const KernelSel& s);    // k_dma_wide.hip: 256x128 and 64x128 tiles, dual gate/up
-const void* kernels_reg(const KernelSel& s);         // k_reg.hip: register-staged tiles
+const void* kernels_reg(const KernelSel& s);         // k_reg.hip: register-staged tiles, every prologue
 const void* kernels_small(const KernelSel& s);       // k_small.hip: small-M and strip kernels
 
 }  // namespace lf

@@ -8,7 +8,7 @@
 
 namespace lf {
 
-enum class Op : int { GemmEpilogue = 0, RmsGemm = 1, RmsSwiglu = 2 };
+enum class Op : int { GemmEpilogue = 0, RmsGemm = 1, RmsSwiglu = 2, LnGemm = 3, BiasGemm = 4 };
 
 // One fused call, already validated.  Pointers are device pointers.
 struct Problem {
@@ -18,7 +18,8 @@ struct Problem {
     const void* W2;     // Wu for RmsSwiglu, else nullptr
     const void* bias;   // [N] or nullptr
     const void* resid;  // [M,N] or nullptr
-    const void* gamma;  // [K] for the RMS ops, else nullptr
+    const void* gamma;  // [K]: gamma of the RMS and LayerNorm ops, the input bias of BiasGemm
+    const void* beta;   // [K] LayerNorm beta or nullptr
     void* Y;            // [M,N]
     int64_t M, N, K;
     float eps;

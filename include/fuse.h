@@ -22,6 +22,23 @@
  *      post, RMSNorm loop nest (mean square, plus eps, rsqrt, times x, times
  *      weight).
  *
+ *  fuse_layernorm_gemm
+ *      Y = act(LayerNorm_{gamma,beta,eps}(X) . W + bias).
+ *      "llm-fusion-compiler": pattern table (layernorm_gemm, LayerNorm + GEMM).
+ *      LayerNorm(X)[m,k] = (X[m,k] - mu[m]) / sqrt(var[m] + eps) * gamma[k]
+ *      + beta[k], mu and var the mean and the biased (centred) variance of
+ *      row m.  Two kernels: the row statistics (written to the library
+ *      workspace, 8 bytes per row), then the GEMM, whose prologue normalises
+ *      each X element on its way to the matrix cores; the normalised
+ *      activation is never written to memory.
+ *
+ *  fuse_gemm_prologue_bias
+ *      Y = act((A + abias) . W + bias) + residual, abias [K] added to every row
+ *      of A inside the reduction.  deplodock post ("A hackable compiler to
+ *      generate efficient fused GPU kernels"), Loop IR worked example
+ *      relu((x + bias) @ w): the add is the prologue inside the reduce, the
+ *      activation the epilogue after it.
+ *
  *  fuse_rmsnorm_gemm_swiglu
  *      H = SiLU(Xhat . Wg) * (Xhat . Wu), Xhat = RMSNorm_{gamma,eps}(X): the
  *      gate and up projections of a SwiGLU FFN sharing one normalised input
@@ -142,6 +159,32 @@ int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
                       int64_t N, int64_t K, int act, int dtype, void* stream);
 
 /*
+ * Y[M,N] = act(LayerNorm_{gamma,beta,eps}(X)[M,K] . W[K,N] + bias[N])
+ *
+ * X, gamma, W, Y required (X and Y may be NULL when M == 0); beta and bias may
+ * be NULL (zero).  The normalised value is formed in float32 from fp64 row
+ * statistics and rounded once to the input dtype as the matrix-core operand.
+ * Uses the split-K workspace of the stream for the statistics (M * 8 bytes).
+ */
+int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta,
+                        float eps, const void* W, const void* bias, void* Y,
+                        int64_t M, int64_t N, int64_t K, int act, int dtype,
+                        void* stream);
+
+/*
+ * Y[M,N] = act((A[M,K] + abias[K]) . W[K,N] + bias[N]) + residual[M,N]
+ *
+ * A, abias, W, Y required (A, Y and residual may be NULL when M == 0); bias
+ * and residual may be NULL.  A + abias is formed in float32 and rounded once
+ * to the input dtype as the matrix-core operand.  Aliasing as for
+ * fuse_gemm_epilogue.
+ */
+int fuse_gemm_prologue_bias(const void* A, const void* abias, const void* W,
+                            const void* bias, const void* residual, void* Y,
+                            int64_t M, int64_t N, int64_t K, int act,
+                            int dtype, void* stream);
+
+/*
  * fuse_rmsnorm_gemm for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, checks and results (bit for bit) as
@@ -179,7 +222,8 @@ int fuse_rmsnorm_gemm_swiglu(const void* X, const void* gamma, float eps,
  * Tile plans.  Each entry point picks a kernel configuration ("plan") from the
  * problem shape.  fuse_plan_name reports the plan a call with these arguments
  * would use (op: 0 = fuse_gemm_epilogue, 1 = fuse_rmsnorm_gemm,
- * 2 = fuse_rmsnorm_gemm_swiglu); it returns "invalid" for an unknown op.
+ * 2 = fuse_rmsnorm_gemm_swiglu, 3 = fuse_layernorm_gemm,
+ * 4 = fuse_gemm_prologue_bias); it returns "invalid" for an unknown op.
  * fuse_set_plan forces one plan by name, "<plan>" or "<plan>:k<S>" for S-way
  * split K, for every later call of this process that the plan fits (a
  * gate/up dual plan only fuse_rmsnorm_gemm_swiglu, the others the two
@@ -192,10 +236,11 @@ const char* fuse_plan_name(int op, int64_t M, int64_t N, int64_t K, int dtype);
 int fuse_set_plan(const char* name);
 
 /*
- * Bytes of split-K workspace (float32 partials plus arrival counters) a call
- * of entry point `op` (numbered as for fuse_plan_name) with these arguments
- * uses under the current plan choice; 0 when its plan does not split K, -1
- * for an unknown op, dtype or invalid shape.  No HIP call.
+ * Bytes of workspace (float32 split-K partials or LayerNorm row statistics,
+ * plus arrival counters) a call of entry point `op` (numbered as for
+ * fuse_plan_name) with these arguments uses under the current plan choice; 0
+ * when it needs none, -1 for an unknown op, dtype or invalid shape.  No HIP
+ * call.
  */
 int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype);
 

@@ -282,3 +282,56 @@ def test_noalloc_rejects_calls_beyond_its_scratch(L):
         assert L.fuse_strerror(E_WORKSPACE) != b"unknown status"
     finally:
         lf.set_plan(None)
+
+
+# --------------------------------------------------------------------------- LayerNorm and prologue-bias entry points
+
+def ln(L, X=A_, g=G_, beta=None, eps=1e-5, W=W_, bias=None, Y=Y_, M=64, N=64, K=64, act=0, dtype=0):
+    return L.fuse_layernorm_gemm(X, g, beta, eps, W, bias, Y, M, N, K, act, dtype, None)
+
+
+def pb(L, A=A_, ab=G_, W=W_, bias=None, res=None, Y=Y_, M=64, N=64, K=64, act=0, dtype=0):
+    return L.fuse_gemm_prologue_bias(A, ab, W, bias, res, Y, M, N, K, act, dtype, None)
+
+
+def test_layernorm_gemm_checks(L):
+    assert ln(L, g=None) == E_NULL
+    assert ln(L, W=None) == E_NULL
+    assert ln(L, M=0, X=None, Y=None) == OK
+    assert ln(L, M=4, N=12) == E_SHAPE
+    assert ln(L, K=0) == E_SHAPE
+    assert ln(L, beta=W2_ + 8) == E_ALIGN
+    assert ln(L, act=4) == E_ENUM
+    assert ln(L, dtype=2) == E_ENUM
+    assert ln(L, eps=float("nan")) == E_EPS
+    assert ln(L, Y=A_) == E_ALIAS
+    assert ln(L, beta=W2_, Y=W2_) == E_ALIAS
+
+
+def test_prologue_bias_gemm_checks(L):
+    assert pb(L, ab=None) == E_NULL
+    assert pb(L, A=None) == E_NULL
+    assert pb(L, M=0, A=None, Y=None) == OK
+    assert pb(L, N=12) == E_SHAPE
+    assert pb(L, ab=G_ + 4) == E_ALIGN
+    assert pb(L, act=-1) == E_ENUM
+    assert pb(L, Y=G_) == E_ALIAS
+    # the residual may be updated in place (same dtype output), not with a float32 output
+    assert pb(L, M=0, A=None, Y=None, res=None) == OK
+    assert pb(L, res=R_, Y=R_ + 16) == E_ALIAS
+
+
+def test_layernorm_and_prologue_bias_plans(L):
+    """Both prologues run in the register-staged kernel; LayerNorm keeps its row
+    statistics (8 bytes per row) in the workspace."""
+    lf.set_plan(None)
+    assert lf.plan_name(3, 4096, 4096, 4096) == "reg_256x256x64"
+    assert lf.plan_name(4, 512, 4096, 4096) == "reg_128x128x64"
+    assert lf.workspace_bytes(3, 2048, 4096, 4096) == (1 << 20) + 2048 * 8
+    assert lf.workspace_bytes(4, 2048, 4096, 4096) == 0
+    lf.set_plan("dma_128x128x64_s4_g2")  # a forced DMA plan does not fit these ops
+    try:
+        assert lf.plan_name(3, 512, 4096, 4096) == "reg_128x128x64"
+        assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
+    finally:
+        lf.set_plan(None)

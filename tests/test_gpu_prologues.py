@@ -1,0 +1,196 @@
+"""LayerNorm -> GEMM and the prologue-bias GEMM against the fp64 oracle (needs
+an MI355X).
+
+fuse_layernorm_gemm: Y = act(LayerNorm(X) W + bias), the layernorm_gemm
+pattern of the "llm-fusion-compiler" pattern table.  fuse_gemm_prologue_bias:
+Y = act((A + b) W + bias) + R, the deplodock post's Loop IR example
+relu((x + bias) @ w).  Both run in the register-staged kernel, forced to each
+of its tiles in turn, over ragged shapes (including K not a multiple of 64),
+every activation and both dtypes, and at full size in the automatic plan; the
+whole output is compared, written into NaN-filled buffers.  Tolerance:
+max_abs_err <= 1.5e-2 and mean_abs_err <= 1.5e-3 (bf16 judged on a float32
+output).  Rows with a mean far from zero check that LayerNorm centres before
+it rounds; operands past the fp16 range check the tile's exact fallback.
+"""
+import numpy as np
+import pytest
+
+import gemm_epilogue_fuse_amd as lf
+import oracle
+import synth
+from parity_util import assert_close, dev_t, say, to64
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-5
+EPS32 = float(np.float32(EPS))
+ACTS = ["none", "relu", "gelu_tanh", "silu"]
+REG_PLANS = ["", "reg_256x256x64", "reg_128x128x64"]
+
+
+@pytest.fixture(params=REG_PLANS)
+def reg_plan(request):
+    lf.set_plan(request.param)
+    yield request.param
+    lf.set_plan(None)
+
+
+def nan_out(shape, dtype):
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda:0")
+
+
+def ln_inputs(M, K, N, dtype, seed, mean_scale=0.0):
+    """X rows N(mu_m, s_m) with per-row scale s_m in [0.5, 2] and mean mu_m =
+    mean_scale * N(0,1) * s_m; gamma = 1 + N(0,0.1), beta ~ N(0,0.1), W ~
+    N(0, 1/sqrt(K)), bias ~ N(0, 0.1)."""
+    g = synth.generator(seed)
+    s = 0.5 + 1.5 * g.random((M, 1))
+    X = (synth.normal(g, (M, K), 1.0) + mean_scale * synth.normal(g, (M, 1), 1.0)) * s
+    gamma = synth.normal(g, (K,), 0.1, 1.0)
+    beta = synth.normal(g, (K,), 0.1)
+    W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))
+    b = synth.normal(g, (N,), 0.1)
+    return {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W),
+                                                     ("bias", b))}
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (1, 8, 64)])
+def test_layernorm_gemm_ragged(reg_plan, dtype, act, M, N, K):
+    import torch
+    say("ln-gemm", reg_plan or "auto", lf.plan_name(3, M, N, K), dtype, act, M, N, K)
+    d = ln_inputs(M, K, N, dtype, seed=81 + M, mean_scale=3.0)
+    t = {k: dev_t(v, dtype) for k, v in d.items()}
+    x = {k: synth.widen(v, dtype) for k, v in d.items()}
+    for with_beta, with_bias in ((True, True), (False, False)):
+        want = oracle.layernorm_gemm(x["X"], x["gamma"], EPS32, x["W"], x["beta"] if with_beta else None,
+                                     x["bias"] if with_bias else None, act)
+        args = (t["X"], t["gamma"], t["W"], EPS, t["beta"] if with_beta else None, t["bias"] if with_bias else None,
+                act)
+        got = to64(lf.layernorm_gemm(*args, out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+        assert_close(got, want, "f32out beta=%d bias=%d" % (with_beta, with_bias))
+        if dtype == synth.F16:
+            got16 = to64(lf.layernorm_gemm(*args, out=nan_out((M, N), torch.float16)))
+            assert_close(got16, want, "f16out")
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_layernorm_gemm_offset_and_range(dtype):
+    """Rows with a mean of 100 standard deviations, rows at 2^-10 and 2^8 scale,
+    and one gamma of 30000 that pushes the normalised value past the fp16
+    maximum (its W row is 1e-5, so outputs stay of unit scale): that tile
+    falls back to the exact path."""
+    import torch
+    M, K, N = 520, 256, 136
+    g = synth.generator(90)
+    Z = synth.normal(g, (M, K), 1.0)
+    scale = np.where(np.arange(M) % 3 == 0, 2.0 ** -10, np.where(np.arange(M) % 3 == 1, 1.0, 2.0 ** 8))[:, None]
+    X = (Z + 100.0 * (np.arange(M) % 2 == 0)[:, None]) * scale
+    gamma = synth.normal(g, (K,), 0.1, 1.0)
+    beta = synth.normal(g, (K,), 0.1)
+    W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))
+    if dtype == synth.F16:
+        gamma[7] = 30000.0
+        W[7] *= 1e-5
+    bits = {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W))}
+    t = {k: dev_t(v, dtype) for k, v in bits.items()}
+    x = {k: synth.widen(v, dtype) for k, v in bits.items()}
+    say("ln-gemm offset/range", dtype, lf.plan_name(3, M, N, K))
+    want = oracle.layernorm_gemm(x["X"], x["gamma"], EPS32, x["W"], x["beta"], None, "gelu_tanh")
+    got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], EPS, t["beta"], None, "gelu_tanh",
+                                 out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+    assert_close(got, want, "offset and range rows")
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_layernorm_gemm_full_size(dtype):
+    """2048 x 4096 -> 4096, GeLU, the automatic plan, whole output."""
+    import torch
+    M, K, N = 2048, 4096, 4096
+    say("ln-gemm full size", dtype, lf.plan_name(3, M, N, K))
+    d = ln_inputs(M, K, N, dtype, seed=91)
+    t = {k: dev_t(v, dtype) for k, v in d.items()}
+    x = {k: synth.widen(v, dtype) for k, v in d.items()}
+    want = oracle.layernorm_gemm(x["X"], x["gamma"], EPS32, x["W"], x["beta"], x["bias"], "gelu_tanh")
+    got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], EPS, t["beta"], t["bias"], "gelu_tanh",
+                                 out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+    assert_close(got, want, "whole output f32out")
+
+
+def pb_inputs(M, K, N, dtype, seed):
+    """A ~ N(0,1) and abias ~ N(0,1) (the page's example draws both from randn),
+    W ~ N(0, 1/64) as in the GEMM + epilogue sweep, bias ~ N(0,0.1), R ~ N(0,1).
+    (x + b has standard deviation sqrt(2); with W ~ N(0, 1/sqrt(K)) the output
+    would have unit scale and the bf16 rounding of the operand alone would put
+    the mean error at the 1.5e-3 bound for any bf16 kernel.)"""
+    g = synth.generator(seed)
+    fields = (("A", synth.normal(g, (M, K), 1.0)), ("abias", synth.normal(g, (K,), 1.0)),
+              ("W", synth.normal(g, (K, N), 1.0 / 64.0)), ("bias", synth.normal(g, (N,), 0.1)),
+              ("R", synth.normal(g, (M, N), 1.0)))
+    return {k: synth.to_bits(v, dtype) for k, v in fields}
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (16, 16, 64)])
+def test_prologue_bias_ragged(reg_plan, dtype, act, M, N, K):
+    import torch
+    say("prologue-bias", reg_plan or "auto", lf.plan_name(4, M, N, K), dtype, act, M, N, K)
+    d = pb_inputs(M, K, N, dtype, seed=95 + K)
+    t = {k: dev_t(v, dtype) for k, v in d.items()}
+    x = {k: synth.widen(v, dtype) for k, v in d.items()}
+    for bias, res in ((True, True), (False, False), (True, False)):
+        want = oracle.prologue_bias_gemm(x["A"], x["abias"], x["W"], x["bias"] if bias else None,
+                                         x["R"] if res else None, act)
+        args = (t["A"], t["abias"], t["W"], t["bias"] if bias else None, t["R"] if res else None, act)
+        got = to64(lf.gemm_prologue_bias(*args, out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+        assert_close(got, want, "f32out bias=%d res=%d" % (bias, res))
+        if dtype == synth.F16:
+            got16 = to64(lf.gemm_prologue_bias(*args, out=nan_out((M, N), torch.float16)))
+            assert_close(got16, want, "f16out bias=%d res=%d" % (bias, res))
+
+
+def test_prologue_bias_worked_example_and_overflow():
+    """The page's relu((x + bias) @ w) at (16, 64) x (64, 16), then a call whose
+    x + b passes the fp16 maximum in a few elements (60000 + 8000; their W rows
+    are 1e-5): the affected tile takes the exact path."""
+    import torch
+    dt = synth.F16
+    g = synth.generator(97)
+    x, ab, w = synth.normal(g, (16, 64), 1.0), synth.normal(g, (64,), 1.0), synth.normal(g, (64, 16), 0.125)
+    bits = {k: synth.to_bits(v, dt) for k, v in (("x", x), ("ab", ab), ("w", w))}
+    t = {k: dev_t(v, dt) for k, v in bits.items()}
+    xv = {k: synth.widen(v, dt) for k, v in bits.items()}
+    say("prologue-bias worked example", lf.plan_name(4, 16, 16, 64))
+    got = to64(lf.gemm_prologue_bias(t["x"], t["ab"], t["w"], act="relu", out=nan_out((16, 16), torch.float16)))
+    assert_close(got, oracle.prologue_bias_gemm(xv["x"], xv["ab"], xv["w"], act_kind="relu"), "worked example")
+    M, K, N = 300, 192, 136
+    A = synth.normal(g, (M, K), 1.0)
+    abias = synth.normal(g, (K,), 1.0)
+    W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))
+    A[5, 3] = 60000.0
+    abias[3] = 8000.0
+    W[3] *= 1e-5
+    bits = {k: synth.to_bits(v, dt) for k, v in (("A", A), ("ab", abias), ("W", W))}
+    t = {k: dev_t(v, dt) for k, v in bits.items()}
+    xv = {k: synth.widen(v, dt) for k, v in bits.items()}
+    want = oracle.prologue_bias_gemm(xv["A"], xv["ab"], xv["W"], act_kind="silu")
+    got = to64(lf.gemm_prologue_bias(t["A"], t["ab"], t["W"], act="silu", out_dtype=torch.float32,
+                                     out=nan_out((M, N), torch.float32)))
+    assert_close(got, want, "x + b past the fp16 maximum")
+
+
+def test_prologue_bias_full_size():
+    """4096^3 GEMM + bias + GeLU with an input bias, the automatic plan, whole output."""
+    import torch
+    M = N = K = 4096
+    say("prologue-bias full size", lf.plan_name(4, M, N, K))
+    d = pb_inputs(M, K, N, synth.F16, seed=99)
+    t = {k: dev_t(v, synth.F16) for k, v in d.items()}
+    x = {k: synth.widen(v, synth.F16) for k, v in d.items()}
+    want = oracle.prologue_bias_gemm(x["A"], x["abias"], x["W"], x["bias"], None, "gelu_tanh")
+    got = to64(lf.gemm_prologue_bias(t["A"], t["abias"], t["W"], t["bias"], None, "gelu_tanh",
+                                     out=nan_out((M, N), torch.float16)))
+    assert_close(got, want, "whole output")
