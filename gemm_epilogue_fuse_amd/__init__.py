@@ -71,6 +71,18 @@ def lib() -> ctypes.CDLL:
         L.fuse_workspace_bytes.argtypes = [ci, i64, i64, i64, ci]
         L.fuse_set_plan.restype = ci
         L.fuse_set_plan.argtypes = [ctypes.c_char_p]
+        L.fuse_tune_set.restype = ci
+        L.fuse_tune_set.argtypes = [ci, i64, i64, i64, ci, ctypes.c_char_p]
+        L.fuse_tune_clear.restype = ci
+        L.fuse_tune_clear.argtypes = []
+        L.fuse_plan_count.restype = ci
+        L.fuse_plan_count.argtypes = []
+        L.fuse_plan_info.restype = ctypes.c_char_p
+        L.fuse_plan_info.argtypes = [ci, ctypes.POINTER(ctypes.c_int32)]
+        L.fuse_plan_applies.restype = ci
+        L.fuse_plan_applies.argtypes = [ci, i64, i64, i64, ci, ctypes.c_char_p]
+        L.fuse_kernel_resources.restype = ci
+        L.fuse_kernel_resources.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(ctypes.c_int32)]
         L.fuse_strerror.restype = ctypes.c_char_p
         L.fuse_strerror.argtypes = [ci]
         L.fuse_version.restype = ci
@@ -78,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.fuse_last_hip_error.restype = ci
         L.fuse_last_hip_error.argtypes = []
         _lib = L
+        # tuned plans from a persistent cache, when the environment names one
+        cache = os.environ.get("LIBFUSE_TUNE_CACHE")
+        if cache and os.path.exists(cache):
+            from . import tuner
+            tuner.load_cache(cache)
     return _lib
 
 

@@ -282,6 +282,57 @@ int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype)
 
 int fuse_set_plan(const char* name) { return lf::set_plan(name) ? FUSE_OK : FUSE_E_ENUM; }
 
+namespace {
+int shape_problem(int op, int64_t M, int64_t N, int64_t K, int dtype, lf::Problem* p) {
+    if (op < 0 || op > 4) return FUSE_E_ENUM;
+    bool bf16 = false, out_f32 = false;
+    if (int rc = check_dtype(dtype, &bf16, &out_f32)) return rc;
+    if (int rc = check_dims(M, N, K)) return rc;
+    *p = lf::Problem{};
+    p->op = static_cast<lf::Op>(op);
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->bf16 = bf16;
+    p->out_f32 = out_f32;
+    return FUSE_OK;
+}
+}  // namespace
+
+int fuse_tune_set(int op, int64_t M, int64_t N, int64_t K, int dtype, const char* plan) {
+    lf::Problem p;
+    if (int rc = shape_problem(op, M, N, K, dtype, &p)) return rc;
+    return lf::tune_set(p, plan) == 0 ? FUSE_OK : FUSE_E_ENUM;
+}
+
+int fuse_tune_clear(void) {
+    lf::tune_clear();
+    return FUSE_OK;
+}
+
+int fuse_plan_count(void) { return lf::plan_count(); }
+
+const char* fuse_plan_info(int i, int32_t* fields) { return fields ? lf::plan_info(i, fields) : nullptr; }
+
+int fuse_plan_applies(int op, int64_t M, int64_t N, int64_t K, int dtype, const char* plan) {
+    lf::Problem p;
+    if (!plan || shape_problem(op, M, N, K, dtype, &p) != FUSE_OK) return 0;
+    return lf::plan_applies(p, plan) ? 1 : 0;
+}
+
+int fuse_kernel_resources(int op, int64_t M, int64_t N, int64_t K, int dtype, int32_t* out) {
+    if (!out) return FUSE_E_NULL;
+    lf::Problem p;
+    if (int rc = shape_problem(op, M, N, K, dtype, &p)) return rc;
+    if (M == 0) return FUSE_E_SHAPE;
+    const hipError_t e = lf::kernel_resources(p, out);
+    if (e != hipSuccess) {
+        t_last_hip = static_cast<int>(e);
+        return FUSE_E_HIP;
+    }
+    return FUSE_OK;
+}
+
 const char* fuse_strerror(int status) {
     switch (status) {
     case FUSE_OK: return "success";

@@ -29,6 +29,8 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <shared_mutex>
+#include <tuple>
 #include <utility>
 #include <vector>
 #include <algorithm>
@@ -136,17 +138,44 @@ int auto_splits(const Plan& pl, const Problem& p) {
     return s;
 }
 
+// Plan `idx` with `s` requested K splits (0 or 1: none), as it runs for `p`
+// (a plan that fits it): the split count is clamped to the K steps, and the
+// small-M kernel takes at least enough splits for chunks of 8 steps.
+Choice pinned(int idx, int s, const Problem& p) {
+    const int64_t nk = p.K / kPlans[idx].bk;
+    if (kPlans[idx].kind == Kind::Dec) {
+        const int64_t lo = (nk + kDecodeMaxSteps - 1) / kDecodeMaxSteps;
+        return {&kPlans[idx], (int)std::min<int64_t>(std::max<int64_t>(s, lo), nk)};
+    }
+    return {&kPlans[idx], (kPlans[idx].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
+}
+
+// Tuned plans: exact (op, M, N, K, dtype) keys filled by fuse_tune_set (the
+// tuner measures every fitting plan and split count and loads its winners
+// from a persistent cache).  Consulted after a forced plan, before the
+// static rules.
+struct TuneKey {
+    int op;
+    int64_t M, N, K;
+    int bf16;
+    bool operator<(const TuneKey& o) const {
+        return std::tie(op, M, N, K, bf16) < std::tie(o.op, o.M, o.N, o.K, o.bf16);
+    }
+};
+std::shared_mutex g_tune_mu;
+std::map<TuneKey, std::pair<int, int>> g_tune;  // key -> (plan index, splits)
+std::atomic<int> g_tune_n{0};
+
+TuneKey tune_key(const Problem& p) { return {(int)p.op, p.M, p.N, p.K, p.bf16 ? 1 : 0}; }
+
 Choice choose(const Problem& p) {
     const int ov = g_override.load(std::memory_order_relaxed);
-    if (ov >= 0 && plan_fits(kPlans[ov], p)) {
-        const int s = g_override_splits.load(std::memory_order_relaxed);
-        const int64_t nk = p.K / kPlans[ov].bk;
-        if (kPlans[ov].kind == Kind::Dec) {
-            // the small-M kernel needs chunks of at most 8 steps
-            const int64_t lo = (nk + kDecodeMaxSteps - 1) / kDecodeMaxSteps;
-            return {&kPlans[ov], (int)std::min<int64_t>(std::max<int64_t>(s, lo), nk)};
-        }
-        return {&kPlans[ov], (kPlans[ov].split && s > 1) ? (int)std::min<int64_t>(s, nk) : 1};
+    if (ov >= 0 && plan_fits(kPlans[ov], p)) return pinned(ov, g_override_splits.load(std::memory_order_relaxed), p);
+    if (g_tune_n.load(std::memory_order_acquire) > 0) {
+        std::shared_lock<std::shared_mutex> lk(g_tune_mu);
+        const auto it = g_tune.find(tune_key(p));
+        if (it != g_tune.end() && plan_fits(kPlans[it->second.first], p))
+            return pinned(it->second.first, it->second.second, p);
     }
     const Plan* pl;
     if (reg_only(p)) {
@@ -341,32 +370,84 @@ const char* plan_name(const Problem& p) {
     return buf;
 }
 
+namespace {
+
+// "<plan>" or "<plan>:k<S>" (S in 1..64, only for plans that split K).
+bool parse_plan(const char* name, int* idx, int* splits) {
+    const char* colon = std::strchr(name, ':');
+    const size_t len = colon ? (size_t)(colon - name) : std::strlen(name);
+    *splits = 0;
+    if (colon) {
+        if (colon[1] != 'k') return false;
+        char* end = nullptr;
+        const long v = std::strtol(colon + 2, &end, 10);
+        if (end == colon + 2 || *end != 0 || v < 1 || v > 64) return false;
+        *splits = (int)v;
+    }
+    for (int i = 0; i < kNumPlans; ++i) {
+        if (std::strlen(kPlans[i].name) == len && std::strncmp(name, kPlans[i].name, len) == 0) {
+            if (*splits > 1 && !kPlans[i].split) return false;
+            *idx = i;
+            return true;
+        }
+    }
+    return false;
+}
+
+}  // namespace
+
 bool set_plan(const char* name) {
     if (name == nullptr || name[0] == 0) {
         g_override.store(-1);
         g_override_splits.store(0);
         return true;
     }
-    // "<plan>" or "<plan>:k<S>", S in 1..64
-    const char* colon = std::strchr(name, ':');
-    const size_t len = colon ? (size_t)(colon - name) : std::strlen(name);
-    int splits = 0;
-    if (colon) {
-        if (colon[1] != 'k') return false;
-        char* end = nullptr;
-        const long v = std::strtol(colon + 2, &end, 10);
-        if (end == colon + 2 || *end != 0 || v < 1 || v > 64) return false;
-        splits = (int)v;
+    int idx = 0, splits = 0;
+    if (!parse_plan(name, &idx, &splits)) return false;
+    g_override_splits.store(splits);
+    g_override.store(idx);
+    return true;
+}
+
+int tune_set(const Problem& p, const char* name) {
+    std::unique_lock<std::shared_mutex> lk(g_tune_mu);
+    if (name == nullptr || name[0] == 0) {
+        g_tune.erase(tune_key(p));
+    } else {
+        int idx = 0, splits = 0;
+        if (!parse_plan(name, &idx, &splits)) return -1;
+        if (!plan_fits(kPlans[idx], p)) return -2;
+        g_tune[tune_key(p)] = {idx, splits};
     }
-    for (int i = 0; i < kNumPlans; ++i) {
-        if (std::strlen(kPlans[i].name) == len && std::strncmp(name, kPlans[i].name, len) == 0) {
-            if (splits > 1 && !kPlans[i].split) return false;
-            g_override_splits.store(splits);
-            g_override.store(i);
-            return true;
-        }
-    }
-    return false;
+    g_tune_n.store((int)g_tune.size(), std::memory_order_release);
+    return 0;
+}
+
+void tune_clear() {
+    std::unique_lock<std::shared_mutex> lk(g_tune_mu);
+    g_tune.clear();
+    g_tune_n.store(0, std::memory_order_release);
+}
+
+int plan_count() { return kNumPlans; }
+
+const char* plan_info(int i, int32_t* f) {
+    if (i < 0 || i >= kNumPlans) return nullptr;
+    const Plan& pl = kPlans[i];
+    f[0] = pl.bm;
+    f[1] = pl.bn;
+    f[2] = pl.bk;
+    f[3] = pl.ns;
+    f[4] = pl.threads();
+    f[5] = pl.split ? 1 : 0;
+    f[6] = pl.dual ? 1 : 0;
+    f[7] = (int)pl.kind;
+    return pl.name;
+}
+
+bool plan_applies(const Problem& p, const char* name) {
+    int idx = 0, splits = 0;
+    return parse_plan(name, &idx, &splits) && plan_fits(kPlans[idx], p);
 }
 
 namespace {
@@ -523,6 +604,22 @@ hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
         return launch_fn(fn, a, nwg, pl.threads(), stream);
     }
     return launch_fn(fn, a, nwg, pl.threads(), stream);
+}
+
+hipError_t kernel_resources(const Problem& p, int32_t* out) {
+    KArgs a;
+    const Choice c = setup(p, a);
+    const void* fn = kernel_for((int)(c.plan - kPlans), p, a.splits > 1);
+    if (fn == nullptr) return hipErrorInvalidDeviceFunction;
+    hipFuncAttributes attr{};
+    const hipError_t e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess) return e;
+    out[0] = (int32_t)attr.sharedSizeBytes;
+    out[1] = c.plan->threads();
+    out[2] = (int32_t)attr.maxThreadsPerBlock;
+    out[3] = (int32_t)attr.numRegs;
+    out[4] = (int32_t)attr.localSizeBytes;
+    return hipSuccess;
 }
 
 }  // namespace lf

@@ -49,4 +49,22 @@ const char* plan_name(const Problem& p);
 // false for an unknown name.
 bool set_plan(const char* name);
 
+// Tuned plan for calls with exactly p's (op, M, N, K, dtype): "<plan>" or
+// "<plan>:k<S>"; nullptr or "" removes the entry.  0 on success, -1 for an
+// unknown name, -2 for a plan that does not fit such calls.
+int tune_set(const Problem& p, const char* name);
+void tune_clear();
+
+// The compiled plans: name and {bm, bn, bk, stages, threads, can split K,
+// dual GEMM, kernel family} (nullptr past the end).
+int plan_count();
+const char* plan_info(int i, int32_t* fields);
+
+// Whether plan `name` ("<plan>" or "<plan>:k<S>") can serve calls like p.
+bool plan_applies(const Problem& p, const char* name);
+
+// Resources of the kernel `launch` would use for p, from the HIP runtime:
+// {LDS bytes, launch threads, max threads per block, registers, scratch bytes}.
+hipError_t kernel_resources(const Problem& p, int32_t* out);
+
 }  // namespace lf

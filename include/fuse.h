@@ -82,8 +82,9 @@
  *              captured into a HIP graph must come after an eager call on the
  *              capturing stream that needed at least as much workspace: an
  *              allocation during capture fails with FUSE_E_HIP
- *              (hipErrorStreamCaptureUnsupported).  This buffer and the plan
- *              override of fuse_set_plan are the library's only state.
+ *              (hipErrorStreamCaptureUnsupported).  This buffer, the plan
+ *              override of fuse_set_plan and the tuned-plan table of
+ *              fuse_tune_set are the library's only state.
  *  Stream      `stream` is a hipStream_t (NULL: the default stream).  Calls are
  *              asynchronous: they return once the kernel is enqueued.
  *  Aliasing    Y must not overlap any input, except Y == residual exactly
@@ -243,6 +244,40 @@ int fuse_set_plan(const char* name);
  * call.
  */
 int64_t fuse_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int dtype);
+
+/*
+ * Tuned plans ("llm-fusion-compiler", Auto-Tuner: a search over tile
+ * configurations under the hardware's limits, timed on the device, with a
+ * persistent cache per pattern, shape and architecture).  The search and the
+ * cache live in the Python tuner (gemm_epilogue_fuse_amd.tuner); the library
+ * holds its results in a process-wide table of exact (op, M, N, K, dtype)
+ * keys, consulted after a plan forced by fuse_set_plan and before the static
+ * shape rules.
+ *
+ * fuse_tune_set     registers `plan` ("<plan>" or "<plan>:k<S>") for calls of
+ *                   entry point `op` (numbered as for fuse_plan_name) with
+ *                   exactly these M, N, K and input dtype; NULL or "" removes
+ *                   the entry.  FUSE_E_ENUM for an unknown plan or one that
+ *                   cannot serve such calls, FUSE_E_SHAPE for a bad shape.
+ * fuse_tune_clear   empties the table.
+ * fuse_plan_count / fuse_plan_info
+ *                   enumerate the compiled plans: the name, and in fields[8]
+ *                   {BM, BN, BK, LDS stages, threads, can split K, dual GEMM,
+ *                   kernel family}; NULL past the end.
+ * fuse_plan_applies 1 if `plan` can serve such calls, else 0.  No HIP call.
+ * fuse_kernel_resources
+ *                   the kernel a call with these arguments would run, as the
+ *                   HIP runtime reports it: out[5] = {LDS bytes, launch
+ *                   threads, max threads per block, registers, scratch bytes
+ *                   per lane}; FUSE_E_HIP where no device is present.
+ * Calls racing with fuse_tune_set see either the old or the new entry.
+ */
+int fuse_tune_set(int op, int64_t M, int64_t N, int64_t K, int dtype, const char* plan);
+int fuse_tune_clear(void);
+int fuse_plan_count(void);
+const char* fuse_plan_info(int i, int32_t* fields);
+int fuse_plan_applies(int op, int64_t M, int64_t N, int64_t K, int dtype, const char* plan);
+int fuse_kernel_resources(int op, int64_t M, int64_t N, int64_t K, int dtype, int32_t* out);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fuse_strerror(int status);
