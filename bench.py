@@ -56,7 +56,7 @@ HEADLINE = "rmsnorm_linear_512x4096x4096_fp16"
 # summaries are used only while these hash to the value recorded with them.
 CSRC = "gemm_epilogue_fuse_amd/csrc/"
 KERNEL_SOURCES = [CSRC + f for f in (
-    "gemm_fused.hip", "kernels.h", "k_dma_square.hip", "k_dma_wide.hip", "k_reg.hip", "k_small.hip",
+    "gemm_fused.hip", "kernels.h", "k_dma_square.hip", "k_dma_wide.hip", "k_dma_pro.hip", "k_reg.hip", "k_small.hip",
     "kernel_dma.h", "kernel_reg.h", "common.h", "kernel_decode.h", "kernel_strip.h", "kernel_wstrip.h",
     "launch.h")]
 

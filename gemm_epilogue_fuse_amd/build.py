@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libfuse.so")
 ARCH = "gfx950"
 
 # One unit per kernel family, so the units compile in parallel.
-SOURCES = ["gemm_fused.hip", "k_dma_square.hip", "k_dma_wide.hip", "k_reg.hip", "k_small.hip", "fuse_api.cpp"]
+SOURCES = ["gemm_fused.hip", "k_dma_square.hip", "k_dma_wide.hip", "k_dma_pro.hip", "k_reg.hip", "k_small.hip",
+           "fuse_api.cpp"]
 HEADERS = ["launch.h", "kernels.h"]
 
 # Packed-fp32 VALU forms are kept out of the device code.

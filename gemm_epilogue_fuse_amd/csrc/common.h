@@ -27,6 +27,7 @@ struct KArgs {
     const uint16_t* gamma;  // [K]: RMSNorm/LayerNorm gamma, or the input bias of the prologue-bias GEMM
     const uint16_t* beta;   // [K] LayerNorm beta (nullptr: zero)
     const float2* stats;    // [M] LayerNorm row statistics (a, b): the operand is a*x + b before gamma, beta
+    const uint32_t* lnstats;  // [M][4] LayerNorm row record of the LDS-DMA kernel (mean, spread, 1/spread)
     void* Y;
     int M, N, K;
     int tiles_m, tiles_n, group_m;

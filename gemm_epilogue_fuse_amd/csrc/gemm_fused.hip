@@ -61,8 +61,8 @@ struct Plan {
 };
 
 constexpr Plan kPlans[] = {
-    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, 2, 2, 1, false, false},  // RMS calls: 4 x 1 waves
-    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, 2, 2, 1, false, true},
+    {"dma_256x256x32_s4", Kind::Dma, 256, 256, 32, 4, 2, 2, 1, false, false},  // every prologue: 4 x 1 waves
+    {"dma_128x128x64_s4", Kind::Dma, 128, 128, 64, 4, 2, 2, 1, false, true},  // bias, LayerNorm: 4 x 1
     {"reg_256x256x64", Kind::Reg, 256, 256, 64, 2, 2, 2, 1, false, false},
     {"reg_128x128x64", Kind::Reg, 128, 128, 64, 2, 2, 2, 1, false, false},
     {"dma_dual_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 4, 1, 1, true, false},
@@ -78,6 +78,7 @@ constexpr Plan kPlans[] = {
     {"wstrip_16x16", Kind::WStrip, 16, 16, 256, 0, 1, 1, 8, false, false},
     {"wstrip_32x16", Kind::WStrip, 32, 16, 256, 0, 1, 1, 8, false, false},
     {"dma_64x128x64_s4_g2", Kind::Dma, 64, 128, 64, 4, 1, 2, 2, false, true},
+    {"dma_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 4, 1, 1, false, true},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 static_assert(kNumPlans == kNumPlanIndices, "plan table and PlanIndex (kernels.h) agree");
@@ -86,12 +87,16 @@ std::atomic<int> g_override{-1};        // forced plan index, -1 = automatic
 std::atomic<int> g_override_splits{0};  // forced split count with a forced plan, 0 = one split
 
 
-// The LayerNorm and input-bias prologues exist in the register-staged kernel only.
-bool reg_only(const Problem& p) { return p.op == Op::LnGemm || p.op == Op::BiasGemm; }
+// The LayerNorm and input-bias prologues run in the register-staged kernel
+// and in the LDS-DMA tiles with 4 x 1 waves (each A row transformed by one
+// wave): 256x256, 256x128 and 128x128.
+bool ln_or_bias(const Problem& p) { return p.op == Op::LnGemm || p.op == Op::BiasGemm; }
+
+bool pro_plan(int idx) { return idx == kDma256 || idx == kDma128 || idx == kDma256x128S4; }
 
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
-    if (reg_only(p) && pl.kind != Kind::Reg) return false;
+    if (ln_or_bias(p) && pl.kind != Kind::Reg && !pro_plan((int)(&pl - kPlans))) return false;
     if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
     if (pl.kind == Kind::Strip && p.op != Op::GemmEpilogue && p.K > dev::kStripMaxK) return false;
     if (pl.kind == Kind::WStrip && p.K > dev::kWStripMaxK) return false;
@@ -178,17 +183,26 @@ Choice choose(const Problem& p) {
             return pinned(it->second.first, it->second.second, p);
     }
     const Plan* pl;
-    if (reg_only(p)) {
+    if (ln_or_bias(p)) {
+        // the 4 x 1 LDS-DMA tiles, largest first while the output still
+        // fills the chip, then 128x128 with split K; K not a multiple of the
+        // K step: the register-staged kernel
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-        return {(t256 >= 224) ? &kPlans[kReg256] : &kPlans[kReg128], 1};
+        const int64_t t256x128 = ((p.M + 255) / 256) * ((p.N + 127) / 128);
+        if (p.K % 64 != 0) return {(t256 >= 224) ? &kPlans[kReg256] : &kPlans[kReg128], 1};
+        pl = (t256 >= 224) ? &kPlans[kDma256] : (t256x128 >= 224) ? &kPlans[kDma256x128S4] : &kPlans[kDma128];
+        return {pl, auto_splits(*pl, p)};
     }
-    if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
+    if (p.op != Op::RmsSwiglu && p.M <= 128 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
         // a few rows and a short K: one workgroup per 16-column strip over
         // all of K (no partial sums cross the device), the whole strip in
         // flight at once (1024x1024: 4.8 us against 6.0 us for the LDS-ring
         // strip).  At longer K the 16-column strips read a quarter of each
         // 128-byte line per workgroup and lose to 64-column tiles with split K.
-        pl = &kPlans[kWStrip16];
+        // Past 64 rows the 32-row strip, which reads each W strip half as
+        // often (cold, 128x1024x1024: 6.5 us against 8.3 us for the small-M
+        // kernel; 64x256x256 GEMM: 3.8 against 4.1 us with 16-row strips).
+        pl = &kPlans[p.M <= 64 ? kWStrip16 : kWStrip32];
     } else if (p.op != Op::RmsSwiglu && p.M <= 32 && p.K <= 1024 && plan_fits(kPlans[kStrip16], p)) {
         pl = &kPlans[kStrip16];
     } else if (p.op != Op::RmsSwiglu && p.M <= kDecodeMaxM && p.K % 64 == 0 &&
@@ -262,12 +276,23 @@ hipError_t zero_words(unsigned* p, size_t bytes, hipStream_t stream) {
 
 // LayerNorm row statistics ("llm-fusion-compiler" pattern table:
 // layernorm_gemm, the statistics pass of a two-kernel LayerNorm + GEMM): one
-// wave per row, mean and centred variance in fp64 over two passes of the row,
-// stored as the fp32 pair (a, b) = (1/sqrt(var + eps), -mean * a), so that the
-// GEMM's prologue forms (a*x + b) * gamma + beta.  Rows are 16-byte aligned
-// (K % 8 == 0), so each lane reads 8 values at a time.
+// wave per row, mean and centred variance in fp64 over two passes of the row.
+// Two forms per row:
+//   rec[m]  16 bytes for the LDS-DMA kernel, which forms
+//           (x - mean) * gamma + beta * s in the input type (s = sqrt(var +
+//           eps)) and scales its accumulator by 1/s: fp16 words 0-2 are the
+//           half pairs (mu_hi, mu_hi), (mu_lo, mu_lo), (s, s) with mean =
+//           mu_hi + mu_lo to about 22 bits; bf16 words 0 and 2 are mean and s
+//           as floats; word 3 is 1/s as a float, negated when var + eps lies
+//           outside the window where those operands keep their precision
+//           (fp16: [2^-24, s below the fp16 maximum]; bf16: [2^-120, 2^100]),
+//           which sends the row's tiles to the exact path;
+//   ab[m]   the fp32 pair (a, b) = (1/s, -mean * a) for the register-staged
+//           kernel, which forms (a*x + b) * gamma + beta in fp32.
+// Rows are 16-byte aligned (K % 8 == 0), so each lane reads 8 values at a time.
 template <bool BF>
-__global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M, int K, float eps, float2* out) {
+__global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M, int K, float eps, dev::u32x4* rec,
+                                                       float2* out) {
     const int lane = threadIdx.x & 63;
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
@@ -291,8 +316,30 @@ __global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M,
     }
     for (int o = 32; o > 0; o >>= 1) v2 += __shfl_xor(v2, o);
     if (lane == 0) {
-        const double a = 1.0 / sqrt(v2 / (double)K + (double)eps);
+        const double ve = v2 / (double)K + (double)eps;
+        const double sd = sqrt(ve);
+        const double a = 1.0 / sd;
         out[m] = make_float2((float)a, (float)(-mu * a));
+        dev::u32x4 r;
+        bool inside;
+        if constexpr (BF) {
+            r[0] = __float_as_uint((float)mu);
+            r[1] = 0u;
+            r[2] = __float_as_uint((float)sd);
+            inside = ve >= 0x1p-120 && ve <= 0x1p100;
+        } else {
+            const _Float16 mh = (_Float16)mu;
+            const _Float16 ml = (_Float16)(mu - (double)mh);
+            const _Float16 sh = (_Float16)sd;
+            const uint32_t bh = __builtin_bit_cast(uint16_t, mh), bl = __builtin_bit_cast(uint16_t, ml);
+            const uint32_t bs = __builtin_bit_cast(uint16_t, sh);
+            r[0] = bh | (bh << 16);
+            r[1] = bl | (bl << 16);
+            r[2] = bs | (bs << 16);
+            inside = ve >= 0x1p-24 && sd < 65504.0;
+        }
+        r[3] = __float_as_uint(inside ? (float)a : -(float)a);
+        rec[m] = r;
     }
 }
 
@@ -354,7 +401,9 @@ const void* kernel_for(int pi, const Problem& p, bool split) {
     case Kind::Dec:
     case Kind::Strip:
     case Kind::WStrip: return kernels_small(s);
-    case Kind::Dma: return (kPlans[pi].bm == kPlans[pi].bn) ? kernels_dma_square(s) : kernels_dma_wide(s);
+    case Kind::Dma:
+        if (pro == dev::kProBias || pro == dev::kProLn || pi == kDma256x128S4) return kernels_dma_pro(s);
+        return (kPlans[pi].bm == kPlans[pi].bn) ? kernels_dma_square(s) : kernels_dma_wide(s);
     }
     return nullptr;
 }
@@ -464,6 +513,7 @@ Choice setup(const Problem& p, KArgs& a) {
     a.gamma = static_cast<const uint16_t*>(p.gamma);
     a.beta = static_cast<const uint16_t*>(p.beta);
     a.stats = nullptr;
+    a.lnstats = nullptr;
     a.Y = p.Y;
     a.M = (int)p.M;
     a.N = (int)p.N;
@@ -496,7 +546,10 @@ size_t split_bytes(const Plan& pl, const Problem& p, const KArgs& a) {
     const size_t tiles = (size_t)a.tiles_m * a.tiles_n;
     const size_t nb = (p.op == Op::RmsSwiglu) ? 2 : 1;
     const size_t acc_floats = nb * pl.bm * pl.bn;
-    const size_t ss_floats = (size_t)pl.threads() * (pl.bm / pl.wm / 32 / pl.kg);
+    // 4 x 1 waves: 256x256 with any prologue, 128x128 with the bias and LayerNorm prologues
+    const int idx = (int)(&pl - kPlans);
+    const int wm = ((idx == kDma256 && p.op != Op::GemmEpilogue) || (idx == kDma128 && ln_or_bias(p))) ? 4 : pl.wm;
+    const size_t ss_floats = (size_t)pl.threads() * (pl.bm / wm / 32 / pl.kg);
     const size_t per_split = (pl.kind == Kind::Dec) ? 256 * 36 : (acc_floats + ss_floats) * sizeof(float);
     return tiles * a.splits * per_split;
 }
@@ -550,15 +603,21 @@ hipError_t get_scratch(hipStream_t stream, float** ws, unsigned** cnt) {
 
 }  // namespace
 
-// Bytes of LayerNorm row statistics a call keeps in the workspace.
-size_t stats_bytes(const Problem& p) { return p.op == Op::LnGemm ? (size_t)p.M * sizeof(float2) : 0; }
+// Bytes of LayerNorm row statistics a call keeps in the workspace: the
+// 16-byte record and the (a, b) pair per row.
+size_t stats_bytes(const Problem& p) { return p.op == Op::LnGemm ? (size_t)p.M * 24 : 0; }
+
+// Split partials rounded up to 256 bytes, so the statistics after them stay aligned.
+size_t split_area(const Plan& pl, const Problem& p, const KArgs& a) {
+    return a.splits > 1 ? (split_bytes(pl, p, a) + 255) / 256 * 256 : 0;
+}
 
 size_t workspace_bytes(const Problem& p) {
     if (p.M == 0) return 0;
     KArgs a;
     const Choice c = setup(p, a);
     if (a.splits == 1 && stats_bytes(p) == 0) return 0;
-    return kCounterBytes + (a.splits > 1 ? split_bytes(*c.plan, p, a) : 0) + stats_bytes(p);
+    return kCounterBytes + split_area(*c.plan, p, a) + stats_bytes(p);
 }
 
 hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
@@ -571,6 +630,7 @@ hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
     const int nwg = a.tiles_m * a.tiles_n * a.splits;
     const void* fn = kernel_for((int)(c.plan - kPlans), p, a.splits > 1);
     if (fn == nullptr) return hipErrorInvalidDeviceFunction;
+    if (noalloc && p.op == Op::LnGemm) return hipErrorInvalidValue;  // its statistics live in the workspace
     if (a.splits > 1 && noalloc) {
         if (kCounterBytes + split_bytes(pl, p, a) > kScratchBytes) return hipErrorInvalidValue;
         const hipError_t e = get_scratch(stream, &a.ws, &a.cnt);
@@ -580,17 +640,20 @@ hipError_t launch(const Problem& p, hipStream_t stream, bool noalloc) {
     if (p.op == Op::LnGemm) {
         // two kernels: the row statistics into the workspace, then the GEMM
         // whose prologue normalises each A element on its way to LDS
+        // (workspace: counters, split partials, then the statistics)
         std::lock_guard<std::mutex> lk(g_ws_mu);
-        float* ws = nullptr;
-        unsigned* cnt = nullptr;
-        hipError_t e = get_workspace(stream, stats_bytes(p), &ws, &cnt);
+        const size_t part = split_area(pl, p, a);
+        hipError_t e = get_workspace(stream, part + stats_bytes(p), &a.ws, &a.cnt);
         if (e != hipSuccess) return e;
-        a.stats = reinterpret_cast<const float2*>(ws);
+        char* st = reinterpret_cast<char*>(a.ws) + part;
+        dev::u32x4* rec = reinterpret_cast<dev::u32x4*>(st);
+        float2* out = reinterpret_cast<float2*>(st + (size_t)a.M * 16);
+        a.lnstats = reinterpret_cast<const uint32_t*>(rec);
+        a.stats = out;
         const uint16_t* X = a.A;
         int M = a.M, K = a.K;
         float eps = a.eps;
-        float2* out = reinterpret_cast<float2*>(ws);
-        void* sargs[] = {&X, &M, &K, &eps, &out};
+        void* sargs[] = {&X, &M, &K, &eps, &rec, &out};
         const void* sfn = p.bf16 ? reinterpret_cast<const void*>(&ln_stats_kernel<true>)
                                  : reinterpret_cast<const void*>(&ln_stats_kernel<false>);
         e = hipLaunchKernel(sfn, dim3((M + 3) / 4), dim3(256), sargs, 0, stream);

@@ -18,10 +18,12 @@
 //                             pointing at k-row (j/4), columns 4(j%4)..+3, lane
 //                             i receives column i at four consecutive k, i.e.
 //                             the K-contiguous operand the matrix core needs.
-//   gamma   [BK]             (RMS only) one 1 KiB slot per stage; with 8 waves
-//                             loaded by wave 0 alone (the other waves issue one
-//                             DMA row fewer per step and wait on counts one
-//                             lower), with 4 waves by every wave.
+//   gamma   [BK]             (with a prologue) one 1 KiB slot per stage for
+//                             gamma (RMSNorm, LayerNorm) or the input bias,
+//                             and a second one for LayerNorm's beta; with 8
+//                             waves loaded by wave 0 alone (the other waves
+//                             issue fewer DMA rows per step and wait on counts
+//                             that much lower), with 4 waves by every wave.
 //
 // Synchronisation per K step: wait until this wave's loads for the step have
 // landed (vmcnt), barrier (every wave's loads landed, every wave done with
@@ -162,15 +164,99 @@ __device__ __forceinline__ void rms_scale_bf16_ahead(u32x4& x, const uint32_t (&
           [h2] "v"(gh[2]), [h3] "v"(gh[3]));
 }
 
+// bf16 pairs {1, 0} and {0, 1}: a two-term dot product against them with an
+// fp32 addend picks one half of x and adds to it in fp32.  The pair is moved
+// into a scalar register by hand: left as a constant, the compiler encodes
+// {1, 0} as the inline constant 1.0, which the bf16 dot instruction does not
+// read as that pair (the results came out wrong).
+constexpr uint32_t kBf16OneLo = 0x00003f80u, kBf16OneHi = 0x3f800000u;
+template <uint32_t V>
+__device__ __forceinline__ bf16x2 bf16_pair() {
+    uint32_t r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(V));
+    return __builtin_bit_cast(bf16x2, r);
+}
+
+// Input-bias prologue: x + b for one 8-value A fragment, rounded once to the
+// 16-bit type (fp16: one packed add; bf16: the sum in fp32, then rounded).
+template <bool BF>
+__device__ __forceinline__ u32x4 bias_add(u32x4 x, u32x4 b) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t xq = x[q];
+        const uint32_t bq = b[q];
+        if constexpr (BF) {
+            const bf16x2 xv = __builtin_bit_cast(bf16x2, xq);
+            const float lo = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneLo>(),
+                                                             __uint_as_float(bq << 16), false);
+            const float hi = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneHi>(),
+                                                             __uint_as_float(bq & 0xffff0000u), false);
+            o[q] = pack2<true>(lo, hi);
+        } else {
+            o[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xq) + __builtin_bit_cast(f16x2, bq));
+        }
+    }
+    return o;
+}
+
+// LayerNorm prologue.  The statistics pass stores per row a 16-byte record:
+// for fp16 inputs the mean as a two-term fp16 sum mu_hi + mu_lo and
+// s = sqrt(var + eps), each as a half pair; for bf16 inputs mu and s as
+// floats (words 0 and 2); in both the float rstd = 1/s in word 3, negative
+// for a row outside the fast path's window.  The operand of x is
+//     round((x - mu) * gamma + beta * s),
+// and rstd multiplies the fp32 accumulator, so that rstd * sum_k op_k W[k,n]
+// is the GEMM of the normalised activation (x - mu) * rstd * gamma + beta.
+// Subtracting the mean before any rounding keeps rows whose mean is large
+// against their spread exact; fp16 does it in packed fp16 (mu_hi, then mu_lo,
+// then one fused multiply-add), bf16 in fp32.
+template <bool BF>
+__device__ __forceinline__ u32x4 ln_apply(u32x4 x, u32x4 g, u32x4 be, u32x4 st) {
+    u32x4 o;
+    if constexpr (BF) {
+        const float mu = __uint_as_float(st[0]), sd = __uint_as_float(st[2]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t xq = x[q], gq = g[q], bq = be[q];
+            const bf16x2 xv = __builtin_bit_cast(bf16x2, xq);
+            const float dlo = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneLo>(), -mu, false);
+            const float dhi = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneHi>(), -mu, false);
+            const float lo = __builtin_fmaf(dlo, __uint_as_float(gq << 16), __uint_as_float(bq << 16) * sd);
+            const float hi = __builtin_fmaf(dhi, __uint_as_float(gq & 0xffff0000u), __uint_as_float(bq & 0xffff0000u) * sd);
+            o[q] = pack2<true>(lo, hi);
+        }
+    } else {
+        const uint32_t w0 = st[0], w1 = st[1], w2 = st[2];
+        const f16x2 mh = __builtin_bit_cast(f16x2, w0), ml = __builtin_bit_cast(f16x2, w1);
+        const f16x2 sd = __builtin_bit_cast(f16x2, w2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t xq = x[q], gq = g[q], bq = be[q];
+            const f16x2 d = (__builtin_bit_cast(f16x2, xq) - mh) - ml;
+            const f16x2 bs = __builtin_bit_cast(f16x2, bq) * sd;
+            o[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(d, __builtin_bit_cast(f16x2, gq), bs));
+        }
+    }
+    return o;
+}
+
 // The workgroup is KG groups of WM x WN waves.  Group g computes the whole
 // BM x BN tile over its own share of every K step (16-wide sub-steps
 // g*KSG .. g*KSG+KSG-1 of each stage), so KG = 2 doubles the waves that keep
 // LDS reads in flight without shrinking the per-wave tile; the groups' sums
 // are added through LDS at the end, after which each wave owns FM/KG of its
 // row blocks.
-template <int BM, int BN, int BK, int NS, int WM, int WN, int KG, bool SRA, bool BF, bool RMS, int NB, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int WM, int WN, int KG, bool SRA, bool BF, int PRO, int NB, bool SPLIT>
 __global__ void __launch_bounds__(WM * WN * KG * 64)
 gemm_dma_kernel(const KArgs p) {
+    constexpr bool RMS = PRO == kProRms;
+    constexpr bool LN = PRO == kProLn;
+    constexpr bool PV = PRO != kProNone;      // a per-k prologue vector (gamma, the input bias) travels with A
+    constexpr int NPV = LN ? 2 : (PV ? 1 : 0);  // 1 KiB slots per stage: gamma or the input bias, then beta
+    constexpr bool ROWSCALE = RMS || LN;      // a per-row factor multiplies the accumulator
+    static_assert(!SRA || PRO == kProNone || RMS, "step read-ahead carries the RMS prologue only");
+    static_assert(PRO <= kProRms || KG == 1, "the bias and LayerNorm prologues use one K group");
     constexpr int NWT = WM * WN;  // waves per K group
     constexpr int NT = NWT * KG * 64;
     constexpr int NW = NT / 64;
@@ -183,13 +269,13 @@ gemm_dma_kernel(const KArgs p) {
     constexpr int A_BYTES = BM * BK * 2;
     constexpr int B_BYTES = BK * BN * 2;
     constexpr int G_OFF = A_BYTES + NB * B_BYTES;
-    constexpr int STAGE = G_OFF + (RMS ? 1024 : 0);
+    constexpr int STAGE = G_OFF + NPV * 1024;
     constexpr int A_LD = A_BYTES / (NT * 16);
     constexpr int B_LD = B_BYTES / (NT * 16);
-    constexpr int LPT = A_LD + NB * B_LD + (RMS ? 1 : 0);  // DMA loads per thread and step (wave 0)
-    constexpr bool G1 = RMS && NW >= 8;                      // gamma loaded by wave 0 alone
+    constexpr int LPT = A_LD + NB * B_LD + NPV;  // DMA loads per thread and step (wave 0)
+    constexpr bool G1 = PV && NW >= 8;           // the prologue vectors loaded by wave 0 alone
     constexpr int NMMA = NB * FM * FN;
-    constexpr int NREAD = FM + 2 * NB * FN + (RMS ? 1 : 0);
+    constexpr int NREAD = FM + 2 * NB * FN + NPV;
     constexpr int WIN = KSG * NMMA;  // matrix-core slots that carry one step's DMA
     static_assert(ACH == 4 || ACH == 8, "BK must be 32 or 64");
     static_assert(BCH >= 16, "BN must be at least 128 for the W swizzle");
@@ -201,7 +287,7 @@ gemm_dma_kernel(const KArgs p) {
     static_assert(NS >= 3, "two stages ahead of the one being read");
     static_assert(SRA || KSG % 2 == 0, "sub-step read-ahead alternates fragment sets within a step");
     static_assert(WIN >= LPT, "one DMA row per matrix-core slot at most");
-    using Store = TileStore<BM, BN, WM * KG, WN, BF, RMS, NB>;
+    using Store = TileStore<BM, BN, WM * KG, WN, BF, ROWSCALE, NB>;
     // The epilogue staging reuses the stages' LDS, extended where it needs more.
     constexpr int SMEM_MAIN = (Store::kBytes > NS * STAGE) ? Store::kBytes : NS * STAGE;
     static_assert(SMEM_MAIN + BM * 4 <= 160 * 1024, "LDS per workgroup");
@@ -226,7 +312,9 @@ gemm_dma_kernel(const KArgs p) {
     const uint32_t w_bytes = (uint32_t)(((size_t)K * N - n0) * 2);
     const i32x4 rsW = rsrc128(p.W + n0, w_bytes);
     const i32x4 rsW2 = rsrc128((NB == 2 ? p.W2 : p.W) + n0, w_bytes);
-    const i32x4 rsG = rsrc128(RMS ? p.gamma : p.W, RMS ? (uint32_t)K * 2u : 0u);
+    const i32x4 rsG = rsrc128(PV ? p.gamma : p.W, PV ? (uint32_t)K * 2u : 0u);
+    // LayerNorm beta; absent, its loads read zeros
+    const i32x4 rsBe = rsrc128((LN && p.beta) ? p.beta : p.W, (LN && p.beta) ? (uint32_t)K * 2u : 0u);
 
     // Loop-invariant per-lane global offsets of the DMA rows (bytes).  Rows
     // past M and columns past N carry the out-of-range bit.
@@ -260,7 +348,8 @@ gemm_dma_kernel(const KArgs p) {
             // with 8 waves one wave loads the step's gamma for the workgroup
             // (the barrier that follows its wait makes it visible to every
             // wave): measured 1-3.5% faster there, 3% slower with 4 waves
-            dma16(rsG, base + (uint32_t)G_OFF, voffG, (uint32_t)k0 * 2u);
+            const int v = d - A_LD - NB * B_LD;  // 0: gamma or the input bias, 1: beta
+            dma16(v ? rsBe : rsG, base + (uint32_t)(G_OFF + v * 1024), voffG, (uint32_t)k0 * 2u);
         }
     };
     // Wait until at most `steps` whole steps of this wave's DMA rows are in
@@ -268,7 +357,7 @@ gemm_dma_kernel(const KArgs p) {
     auto wait_steps = [&](auto STEPS) {
         constexpr int n = decltype(STEPS)::value;
         if (!G1 || wave == 0) wait_vmcnt<n * LPT>();
-        else wait_vmcnt<n * (G1 ? LPT - 1 : LPT)>();
+        else wait_vmcnt<n * (G1 ? LPT - NPV : LPT)>();
     };
     auto issue = [&](int s, int k0) {
 #pragma unroll
@@ -292,6 +381,13 @@ gemm_dma_kernel(const KArgs p) {
     int arow[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + (lane & 31);
+    // LayerNorm: this lane's row record of each row block (rows past M: zeros)
+    u32x4 lnst[LN ? FM : 1];
+#pragma unroll
+    for (int i = 0; i < (LN ? FM : 1); ++i) {
+        lnst[i] = u32x4{0u, 0u, 0u, 0u};
+        if (LN && m0 + arow[i] < M) lnst[i] = *reinterpret_cast<const u32x4*>(p.lnstats + 4 * (size_t)(m0 + arow[i]));
+    }
     const int bkr = 8 * (lane >> 5) + ((lane >> 2) & 3);  // k-row within a 16-k step
     const int bcol = wn * TN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
@@ -306,7 +402,8 @@ gemm_dma_kernel(const KArgs p) {
     struct Frags {
         u32x4 a[KH][FM];
         u32x4 b[KH][NB][FN];  // k 0..3 of the lane's group from the first transposing read, 4..7 from the second
-        u32x4 g[KH];
+        u32x4 g[KH];          // gamma or the input bias
+        u32x4 be[KH];         // LayerNorm beta
     };
     // One LDS read of local sub-step ls of stage s into slot h of a set.
     // With sub-step read-ahead pieces come in the order the matrix cores
@@ -314,14 +411,21 @@ gemm_dma_kernel(const KArgs p) {
     // (operand, column block), then A blocks 1..FM-1.  With step read-ahead
     // A blocks and gamma come first, so they can be scaled early.
     constexpr int NRB = 2 * NB * FN;  // transposing reads per sub-step
-    constexpr int G0 = RMS ? 1 : 0;
+    constexpr int G0 = NPV;
     // With sub-step read-ahead and enough matrix-core slots per sub-step,
     // the next sub-step's A blocks and gamma are read first and scaled a
     // few slots later, while this sub-step's matrix-core work runs, so no
     // matrix-core instruction waits on the scaling.  AHEAD_SLOT is the slot
-    // that scales them.
-    constexpr int AHEAD_SLOT = FM + G0 + 2;
-    constexpr bool AHEAD = RMS && !SRA && AHEAD_SLOT < NMMA;
+    // that scales them (the bias and LayerNorm prologues take the last slot
+    // when a sub-step has too few, once every A and vector read is issued).
+    constexpr int AHEAD_SLOT = RMS ? FM + G0 + 2 : (FM + G0 + 2 < NMMA ? FM + G0 + 2 : NMMA - 1);
+    constexpr bool AHEAD = PV && !SRA && AHEAD_SLOT < NMMA && AHEAD_SLOT >= FM + G0;
+    // The prologue of A block i of a fragment set (bias, LayerNorm; RMS keeps its own forms).
+    auto pro_apply = [&](u32x4 a, const Frags& f, int h, int i) -> u32x4 {
+        if constexpr (PRO == kProBias) return bias_add<BF>(a, f.g[h]);
+        else if constexpr (LN) return ln_apply<BF>(a, f.g[h], f.be[h], lnst[i]);
+        else return rms_scale<BF>(a, f.g[h], ss[i]);
+    };
     auto read_piece = [&](Frags& f, int s, int ls, int h, int r) {
         const int ks = g * KSG + ls;
         const int sbase = s * STAGE;
@@ -335,8 +439,10 @@ gemm_dma_kernel(const KArgs p) {
             const int i = (r == 0) ? 0 : r - G0 - NRB;
             const int off = sbase + arow[i] * (BK * 2) + ((lc ^ swz_a<ACH>(arow[i])) << 4);
             f.a[h][i] = *reinterpret_cast<const u32x4*>(smem + off);
-        } else if (RMS && r == 1) {
-            f.g[h] = *reinterpret_cast<const u32x4*>(smem + sbase + G_OFF + (lc << 4));
+        } else if (PV && r >= 1 && r <= G0) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + sbase + G_OFF + (r - 1) * 1024 + (lc << 4));
+            if (r == 1) f.g[h] = v;
+            else f.be[h] = v;
         } else {
             const int t = r - 1 - G0;
             const int o = t / (2 * FN), j = (t / 2) % FN, q = t & 1;
@@ -355,8 +461,8 @@ gemm_dma_kernel(const KArgs p) {
     // (see below).
     auto mma = [&](Frags& cur, int h, int m) {
         const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
-        if constexpr (RMS && !SRA && !AHEAD)
-            if (o == 0 && j == 0) cur.a[h][i] = rms_scale<BF>(cur.a[h][i], cur.g[h], ss[i]);
+        if constexpr (PV && !SRA && !AHEAD)
+            if (o == 0 && j == 0) cur.a[h][i] = pro_apply(cur.a[h][i], cur, h, i);
         acc[o][i][j] = mfma32<BF>(cur.a[h][i], cur.b[h][o][j], acc[o][i][j]);
     };
 
@@ -467,7 +573,7 @@ gemm_dma_kernel(const KArgs p) {
         for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, 0, r);
         if constexpr (AHEAD) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) F0.a[0][i] = rms_scale<BF>(F0.a[0][i], F0.g[0], ss[i]);
+            for (int i = 0; i < FM; ++i) F0.a[0][i] = pro_apply(F0.a[0][i], F0, 0, i);
         }
         // scratch of the bf16 one-slot-ahead scaling, live across the loop
         float sct[8];
@@ -510,7 +616,7 @@ gemm_dma_kernel(const KArgs p) {
                     if (m == AHEAD_SLOT) {
                         // all blocks in one slot: independent chains the
                         // scheduler can interleave
-                        if constexpr (BF) {
+                        if constexpr (BF && RMS) {
                             uint32_t gl[4], gh[4];
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
@@ -521,7 +627,7 @@ gemm_dma_kernel(const KArgs p) {
                             for (int i = 0; i < FM; ++i) rms_scale_bf16_ahead(nxt.a[0][i], gl, gh, ss[i], sct);
                         } else {
 #pragma unroll
-                            for (int i = 0; i < FM; ++i) nxt.a[0][i] = rms_scale<BF>(nxt.a[0][i], nxt.g[0], ss[i]);
+                            for (int i = 0; i < FM; ++i) nxt.a[0][i] = pro_apply(nxt.a[0][i], nxt, 0, i);
                         }
                     }
                 if constexpr (do_dma) {
@@ -731,15 +837,21 @@ gemm_dma_kernel(const KArgs p) {
     }
 
     float* rs = reinterpret_cast<float*>(smem + SMEM_MAIN);
-    if constexpr (RMS) {
+    if constexpr (PV) {
         // lanes l and l+32 hold the two k-halves of row l%32 of each block
         bool bad = false;
 #pragma unroll
         for (int i = 0; i < FMO; ++i) {
-            const float s = sso[i] + __shfl_xor(sso[i], 32);
             const int rl = wme * TME + i * 32 + (lane & 31);
-            if (wn == 0 && lane < 32) rs[rl] = 1.0f / sqrtf(s / (float)K + p.eps);
-            bad |= m0 + rl < M && rms_outside<BF>(s, K, p.eps);
+            if constexpr (RMS) {
+                const float s = sso[i] + __shfl_xor(sso[i], 32);
+                if (wn == 0 && lane < 32) rs[rl] = 1.0f / sqrtf(s / (float)K + p.eps);
+                bad |= m0 + rl < M && rms_outside<BF>(s, K, p.eps);
+            } else if constexpr (LN) {
+                const float rstd = __uint_as_float(lnst[i][3]);
+                if (wn == 0 && lane < 32) rs[rl] = fabsf(rstd);
+                bad |= m0 + rl < M && !(rstd > 0.0f);
+            }
         }
         // an operand that overflowed leaves a non-finite accumulator (and
         // the sum of non-finite and finite values is never finite)
@@ -755,7 +867,7 @@ gemm_dma_kernel(const KArgs p) {
         bad |= !__builtin_isfinite(t);
         __syncthreads();
         if (__syncthreads_or(bad)) {
-            prologue_exact_tile<BF, NB, NT, BN>(p, smem, m0, BM, n0);
+            prologue_exact_tile<BF, NB, NT, BN, PRO>(p, smem, m0, BM, n0);
             return;
         }
     }

@@ -25,7 +25,8 @@ enum PlanIndex : int {
     kWStrip16 = 14,
     kWStrip32 = 15,
     kDma64x128G2 = 16,
-    kNumPlanIndices = 17
+    kDma256x128S4 = 17,
+    kNumPlanIndices = 18
 };
 
 // Which instantiation of a plan's kernel a call needs.
@@ -44,5 +45,6 @@ const void* kernels_dma_square(const KernelSel& s);  // k_dma_square.hip: 128x12
 const void* kernels_dma_wide(const KernelSel& s);    // k_dma_wide.hip: 256x128 and 64x128 tiles, dual gate/up
 const void* kernels_reg(const KernelSel& s);         // k_reg.hip: register-staged tiles, every prologue
 const void* kernels_small(const KernelSel& s);       // k_small.hip: small-M and strip kernels
+const void* kernels_dma_pro(const KernelSel& s);     // k_dma_pro.hip: 4 x 1 wave tiles, input-bias and LayerNorm
 
 }  // namespace lf

@@ -12,7 +12,8 @@ heuristic fallback where no device can time them.  Here:
   most 1024 threads, whole 64-wide waves) and the 64 MiB split-K workspace
   are checked against what the HIP runtime reports for each candidate's
   kernel (``fuse_kernel_resources``) and ``fuse_workspace_bytes``;
-* each candidate is timed as a HIP graph of back-to-back calls;
+* each candidate is timed as a HIP graph of back-to-back calls, over enough
+  input sets that consecutive calls miss the last-level cache;
 * the cache maps "op|M|N|K|dtype|arch" to the winning plan (with its time,
   the static choice's time and every candidate's), and ``load_cache``
   registers the entries of the running architecture with
@@ -161,6 +162,13 @@ def heuristic(op: int, M: int, N: int, K: int, dtype: int = F16) -> str:
 
 # ----------------------------------------------------------------------------- timing on the device
 
+ROTATE_BYTES = 640 << 20  # input footprint of a timing: past the 256 MB last-level cache
+
+
+def _set_bytes(op, M, N, K):
+    return 2 * (M * K + K * N * (2 if op == 2 else 1) + M * N + 2 * K + N)
+
+
 def _inputs(op, M, N, K, dtype, nsets=2):
     import torch
     tdt = torch.bfloat16 if (dtype & 0xff) == BF16 else torch.float16
@@ -231,9 +239,11 @@ def _time_us(calls, launches, replays=3):
 
 
 def tune(op: int, M: int, N: int, K: int, dtype: int = F16, launches: int = 20, path: str | None = None,
-         write: bool = True, max_candidates: int | None = None) -> dict:
+         write: bool = True, max_candidates: int | None = None, cold: bool = True) -> dict:
     """Time every candidate plan for the call, register the fastest and (with
-    `write`) store it in the cache.  Without a GPU: the heuristic choice."""
+    `write`) store it in the cache.  `cold` rotates over enough input sets that
+    consecutive calls miss the last-level cache (a model's layer after layer);
+    otherwise two sets.  Without a GPU: the heuristic choice."""
     import torch
     if not torch.cuda.is_available():
         return {"plan": heuristic(op, M, N, K, dtype), "source": "heuristic"}
@@ -241,7 +251,9 @@ def tune(op: int, M: int, N: int, K: int, dtype: int = F16, launches: int = 20, 
     cands = candidates(op, M, N, K, dtype)
     if max_candidates is not None:
         cands = ([default] + [c for c in cands if c != default])[:max_candidates]
-    sets = _inputs(op, M, N, K, dtype)
+    nsets = max(2, min(64, -(-ROTATE_BYTES // _set_bytes(op, M, N, K)))) if cold else 2
+    sets = _inputs(op, M, N, K, dtype, nsets)
+    launches = max(launches, nsets)
     times = {}
     try:
         for c in cands:
@@ -256,7 +268,7 @@ def tune(op: int, M: int, N: int, K: int, dtype: int = F16, launches: int = 20, 
         set_tuned(op, M, N, K, dtype, None)
     best = min(times, key=times.get)
     set_tuned(op, M, N, K, dtype, best)
-    ent = {"plan": best, "us": round(times[best], 3), "default_plan": default,
+    ent = {"plan": best, "us": round(times[best], 3), "default_plan": default, "cold": cold,
            "default_us": round(times[default], 3) if default in times else None,
            "candidates": {k: round(v, 3) for k, v in sorted(times.items(), key=lambda kv: kv[1])},
            "tuned_at": time.strftime("%Y-%m-%dT%H:%M:%S")}

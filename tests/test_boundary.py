@@ -140,7 +140,9 @@ def test_plans(L):
     assert lf.plan_name(1, 8, 1024, 896) == "strip_16x16"       # K % 256 != 0: the LDS-ring strip
     assert lf.plan_name(1, 1, 4096, 4096) == "dec_32x64:k8"      # long K: 32x64 tiles, K chunks of 8 steps
     assert lf.plan_name(1, 32, 4096, 4096) == "dec_32x64:k8"
-    assert lf.plan_name(1, 33, 1024, 1024) == "dec_32x64:k2"
+    assert lf.plan_name(1, 33, 1024, 1024) == "wstrip_16x16"      # up to 64 rows: 16-row whole strips
+    assert lf.plan_name(1, 65, 1024, 1024) == "wstrip_32x16"      # 65..128 rows: 32-row whole strips
+    assert lf.plan_name(1, 33, 2048, 2048) == "dec_32x64:k4"
     # 33 rows re-read a 32 MiB W twice: a split tile takes over; 128x128 would split
     # K eight ways (8 steps per split), so the 64x128 tile splits it four ways
     assert lf.plan_name(1, 33, 4096, 4096) == "dma_64x128x64_s4_g2:k8"
@@ -163,7 +165,8 @@ def test_plans(L):
     finally:
         lf.set_plan(None)
     assert lf.plan_name(1, 64, 64, 64) == "dec_32x64"
-    assert lf.plan_name(1, 128, 1024, 1024) == "dec_32x64:k2"   # 4 x 16 tiles, two K chunks of 8 steps
+    assert lf.plan_name(1, 128, 1024, 1024) == "wstrip_32x16"   # 4 row tiles of 32, 64 strips, all of K
+    assert lf.plan_name(1, 128, 1024, 1152) == "dec_32x64:k3"   # K % 256 != 0: the small-M kernel
     assert lf.plan_name(1, 129, 4096, 4096) == "dma_64x128x64_s4_g2:k2"  # beyond decode rows: 3 x 32 tiles of 64x128
     assert lf.plan_name(2, 1, 256, 4096) == "dma_dual_256x128x32_s4"     # the dual GEMM has no small-M kernel
     # forced split counts
@@ -322,16 +325,32 @@ def test_prologue_bias_gemm_checks(L):
 
 
 def test_layernorm_and_prologue_bias_plans(L):
-    """Both prologues run in the register-staged kernel; LayerNorm keeps its row
-    statistics (8 bytes per row) in the workspace."""
+    """Both prologues run in the 4 x 1 wave LDS-DMA tiles where K is a multiple
+    of 64 (256x256 while it fills the chip, then 256x128, then 128x128 with
+    split K), else in the register-staged kernel; LayerNorm keeps its row
+    statistics (24 bytes per row) in the workspace after any split partials."""
+    MiB = 1 << 20
     lf.set_plan(None)
-    assert lf.plan_name(3, 4096, 4096, 4096) == "reg_256x256x64"
-    assert lf.plan_name(4, 512, 4096, 4096) == "reg_128x128x64"
-    assert lf.workspace_bytes(3, 2048, 4096, 4096) == (1 << 20) + 2048 * 8
+    assert lf.plan_name(3, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(3, 2048, 4096, 4096) == "dma_256x128x32_s4"
+    assert lf.plan_name(4, 512, 4096, 4096) == "dma_128x128x64_s4:k2"
+    assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
+    assert lf.plan_name(3, 4096, 4096, 4104) == "reg_256x256x64"
+    assert lf.workspace_bytes(3, 4096, 4096, 4096) == MiB + 4096 * 24
+    assert lf.workspace_bytes(3, 2048, 4096, 4096) == MiB + 2048 * 24
     assert lf.workspace_bytes(4, 2048, 4096, 4096) == 0
-    lf.set_plan("dma_128x128x64_s4_g2")  # a forced DMA plan does not fit these ops
+    split = 128 * 2 * (128 * 128 + 256) * 4
+    assert lf.workspace_bytes(4, 512, 4096, 4096) == MiB + split
+    assert lf.workspace_bytes(3, 512, 4096, 4096) == MiB + split + 512 * 24
+    lf.set_plan("dma_128x128x64_s4_g2")  # a forced plan without the prologues falls back to the automatic one
     try:
-        assert lf.plan_name(3, 512, 4096, 4096) == "reg_128x128x64"
+        assert lf.plan_name(3, 512, 4096, 4096) == "dma_128x128x64_s4:k2"
+        assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
+    finally:
+        lf.set_plan(None)
+    lf.set_plan("dma_256x128x32_s4:k3")
+    try:
+        assert lf.plan_name(3, 300, 392, 320) == "dma_256x128x32_s4:k3"
         assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
     finally:
         lf.set_plan(None)

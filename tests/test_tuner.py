@@ -47,10 +47,15 @@ def test_candidates_follow_each_ops_constraints():
     # split labels clamp like the library: the small-M kernel needs chunks of at most 8 steps
     c = tuner.candidates(1, 32, 4096, 4096)
     assert "dec_32x64:k8" in c and "dec_32x64:k2" not in c
-    # the gate/up pair only has the dual plans; LayerNorm and the input bias only register plans
+    # the gate/up pair only has the dual plans; LayerNorm and the input bias the register-staged
+    # plans and the 4 x 1 wave LDS-DMA tiles
     assert all("dual" in x for x in tuner.candidates(2, 512, 1024, 1024))
-    assert all(x.startswith("reg_") for x in tuner.candidates(3, 512, 1024, 1024))
-    assert all(x.startswith("reg_") for x in tuner.candidates(4, 512, 1024, 1024))
+    pro_tiles = ("reg_", "dma_256x256x32_s4", "dma_256x128x32_s4", "dma_128x128x64_s4")
+    for op in (3, 4):
+        c = tuner.candidates(op, 512, 1024, 1024)
+        assert all(x.split(":")[0] in ("dma_256x256x32_s4", "dma_256x128x32_s4", "dma_128x128x64_s4")
+                   or x.startswith("reg_") for x in c), c
+        assert all(any(x.startswith(t) for x in c) for t in pro_tiles), c
     # enumerating candidates leaves no entry behind
     assert lf.plan_name(1, 32, 4096, 4096) == tuner.heuristic(1, 32, 4096, 4096)
 
