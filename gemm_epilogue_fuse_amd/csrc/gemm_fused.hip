@@ -78,7 +78,7 @@ constexpr Plan kPlans[] = {
     {"wstrip_16x16", Kind::WStrip, 16, 16, 256, 0, 1, 1, 8, false, false},
     {"wstrip_32x16", Kind::WStrip, 32, 16, 256, 0, 1, 1, 8, false, false},
     {"dma_64x128x64_s4_g2", Kind::Dma, 64, 128, 64, 4, 1, 2, 2, false, true},
-    {"dma_256x128x32_s4", Kind::Dma, 256, 128, 32, 4, 4, 1, 1, false, true},
+    {"dma_256x128x64_s3", Kind::Dma, 256, 128, 64, 3, 4, 1, 1, false, true},
 };
 constexpr int kNumPlans = sizeof(kPlans) / sizeof(kPlans[0]);
 static_assert(kNumPlans == kNumPlanIndices, "plan table and PlanIndex (kernels.h) agree");
@@ -89,14 +89,18 @@ std::atomic<int> g_override_splits{0};  // forced split count with a forced plan
 
 // The LayerNorm and input-bias prologues run in the register-staged kernel
 // and in the LDS-DMA tiles with 4 x 1 waves (each A row transformed by one
-// wave): 256x256, 256x128 and 128x128.
+// wave): 256x256, 256x128 and 128x128.  The input bias, one packed add per
+// pair of fp16 values, also runs in the 8-wave 256x256 and 256x128 tiles.
 bool ln_or_bias(const Problem& p) { return p.op == Op::LnGemm || p.op == Op::BiasGemm; }
 
-bool pro_plan(int idx) { return idx == kDma256 || idx == kDma128 || idx == kDma256x128S4; }
+bool pro_plan(int idx, const Problem& p) {
+    if (idx == kDma256 || idx == kDma128 || idx == kDma256x128S3) return true;
+    return p.op == Op::BiasGemm && (idx == kDma256W8 || idx == kDma256x128x64W8);
+}
 
 bool plan_fits(const Plan& pl, const Problem& p) {
     if (pl.dual != (p.op == Op::RmsSwiglu)) return false;
-    if (ln_or_bias(p) && pl.kind != Kind::Reg && !pro_plan((int)(&pl - kPlans))) return false;
+    if (ln_or_bias(p) && pl.kind != Kind::Reg && !pro_plan((int)(&pl - kPlans), p)) return false;
     if (pl.kind != Kind::Reg && (p.K % pl.bk) != 0) return false;
     if (pl.kind == Kind::Strip && p.op != Op::GemmEpilogue && p.K > dev::kStripMaxK) return false;
     if (pl.kind == Kind::WStrip && p.K > dev::kWStripMaxK) return false;
@@ -190,7 +194,11 @@ Choice choose(const Problem& p) {
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         const int64_t t256x128 = ((p.M + 255) / 256) * ((p.N + 127) / 128);
         if (p.K % 64 != 0) return {(t256 >= 224) ? &kPlans[kReg256] : &kPlans[kReg128], 1};
-        pl = (t256 >= 224) ? &kPlans[kDma256] : (t256x128 >= 224) ? &kPlans[kDma256x128S4] : &kPlans[kDma128];
+        if (p.op == Op::BiasGemm)
+            // the plain GEMM's 8-wave tiles (cold 4096^3: 256x256 with 8 waves ahead of 4 x 1 waves)
+            pl = (t256 >= 224) ? &kPlans[kDma256W8] : (t256x128 >= 224) ? &kPlans[kDma256x128x64W8] : &kPlans[kDma128];
+        else
+            pl = (t256 >= 224) ? &kPlans[kDma256] : (t256x128 >= 224) ? &kPlans[kDma256x128S3] : &kPlans[kDma128];
         return {pl, auto_splits(*pl, p)};
     }
     if (p.op != Op::RmsSwiglu && p.M <= 128 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
@@ -214,7 +222,11 @@ Choice choose(const Problem& p) {
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         const int64_t t256x128 = ((p.M + 255) / 256) * ((p.N + 127) / 128);
         if (t256 >= 224) {
-            pl = (p.K % 32 == 0) ? &kPlans[kDma256] : &kPlans[kReg256];
+            // the plain GEMM on 8 waves of 128x64 (cold 4096^3: 116-122 us
+            // against 124-135 us with 4 waves); with RMSNorm 4 x 1 waves, so
+            // each row is scaled once
+            const PlanIndex big = (p.op == Op::GemmEpilogue) ? kDma256W8 : kDma256;
+            pl = (p.K % 32 == 0) ? &kPlans[big] : &kPlans[kReg256];
         } else if (t256x128 >= 224 && p.K % 64 == 0) {
             // Enough 256x128 tiles to fill the chip without splitting K: 8
             // waves of 64x64 keep LDS reads in flight, and the taller tile
@@ -297,21 +309,39 @@ __global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M,
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
     const uint16_t* x = X + (size_t)m * K;
-    double s = 0.0;
-    for (int k = 8 * lane; k < K; k += 512) {
-        const dev::u32x4 v = *reinterpret_cast<const dev::u32x4*>(x + k);
+    // A lane holds R 16-byte chunks at once, all loads in flight together:
+    // rows of up to 512 R values are read from memory once for both passes.
+    constexpr int R = 8;
+    dev::u32x4 v[R];
+    auto load = [&](int base) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s += (double)dev::lo_f32<BF>(v[q]) + (double)dev::hi_f32<BF>(v[q]);
+        for (int c = 0; c < R; ++c) {
+            const int k = base + 8 * (lane + 64 * c);
+            v[c] = k < K ? *reinterpret_cast<const dev::u32x4*>(x + k) : dev::u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const bool held = K <= 512 * R;
+    double s = 0.0;
+    for (int base = 0; base < K; base += 512 * R) {
+        load(base);
+#pragma unroll
+        for (int c = 0; c < R; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s += (double)dev::lo_f32<BF>(v[c][q]) + (double)dev::hi_f32<BF>(v[c][q]);
     }
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     const double mu = s / (double)K;
     double v2 = 0.0;
-    for (int k = 8 * lane; k < K; k += 512) {
-        const dev::u32x4 v = *reinterpret_cast<const dev::u32x4*>(x + k);
+    for (int base = 0; base < K; base += 512 * R) {
+        if (!held) load(base);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const double d0 = (double)dev::lo_f32<BF>(v[q]) - mu, d1 = (double)dev::hi_f32<BF>(v[q]) - mu;
-            v2 = fma(d0, d0, fma(d1, d1, v2));
+        for (int c = 0; c < R; ++c) {
+            if (base + 8 * (lane + 64 * c) >= K) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double d0 = (double)dev::lo_f32<BF>(v[c][q]) - mu, d1 = (double)dev::hi_f32<BF>(v[c][q]) - mu;
+                v2 = fma(d0, d0, fma(d1, d1, v2));
+            }
         }
     }
     for (int o = 32; o > 0; o >>= 1) v2 += __shfl_xor(v2, o);
@@ -402,7 +432,7 @@ const void* kernel_for(int pi, const Problem& p, bool split) {
     case Kind::Strip:
     case Kind::WStrip: return kernels_small(s);
     case Kind::Dma:
-        if (pro == dev::kProBias || pro == dev::kProLn || pi == kDma256x128S4) return kernels_dma_pro(s);
+        if (pro == dev::kProBias || pro == dev::kProLn || pi == kDma256x128S3) return kernels_dma_pro(s);
         return (kPlans[pi].bm == kPlans[pi].bn) ? kernels_dma_square(s) : kernels_dma_wide(s);
     }
     return nullptr;

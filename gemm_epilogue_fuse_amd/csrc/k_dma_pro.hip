@@ -3,7 +3,10 @@
 // the prologue (input bias, LayerNorm) in exactly one wave.  256x256 (64 x 256
 // per wave), 128x128 with a 64-wide K step (32 x 128 per wave, with or
 // without the split-K exchange) for the bias and LayerNorm GEMMs, and
-// 256x128 (64 x 128 per wave) for every prologue.
+// 256x128 with a 64-wide K step in 3 stages (64 x 128 per wave) for every
+// prologue.  Also the input bias in the plain GEMM's 8-wave tiles (256x256
+// as 2 x 4 waves, 256x128 as 4 x 2), where its one add per value costs
+// little even though two or four waves repeat it for each row.
 #include "kernels.h"
 #include "kernel_dma.h"
 
@@ -25,9 +28,19 @@ const void* pro(const KernelSel& s) {
                        ? reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 4, 1, 1, false, BF, PRO, 1, true>)
                        : reinterpret_cast<const void*>(&gemm_dma_kernel<128, 128, 64, 4, 4, 1, 1, false, BF, PRO, 1, false>);
         return nullptr;
-    case kDma256x128S4:
-        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 4, 4, 1, 1, false, BF, PRO, 1, true>)
-                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 4, 4, 1, 1, false, BF, PRO, 1, false>);
+    case kDma256x128S3:
+        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 1, 1, false, BF, PRO, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 1, 1, false, BF, PRO, 1, false>);
+    case kDma256W8:
+        if constexpr (PRO == kProBias)
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 256, 32, 4, 2, 4, 1, false, BF, PRO, 1, false>);
+        return nullptr;
+    case kDma256x128x64W8:
+        if constexpr (PRO == kProBias)
+            return s.split
+                       ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, PRO, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, PRO, 1, false>);
+        return nullptr;
     default:
         return nullptr;
     }

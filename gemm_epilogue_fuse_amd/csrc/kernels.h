@@ -25,7 +25,7 @@ enum PlanIndex : int {
     kWStrip16 = 14,
     kWStrip32 = 15,
     kDma64x128G2 = 16,
-    kDma256x128S4 = 17,
+    kDma256x128S3 = 17,
     kNumPlanIndices = 18
 };
 

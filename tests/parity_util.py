@@ -66,7 +66,7 @@ PLANS = ["dma_256x256x32_s4", "dma_128x128x64_s4", "reg_256x256x64", "reg_128x12
          "dma_128x128x32_s8_g2", "dma_128x128x32_s8_g2:k2", "dec_32x64", "dec_32x64:k3",
          "strip_16x16", "strip_32x16", "dma_256x128x32_s6_w8", "dma_256x128x32_s6_w8:k3",
          "dma_256x128x64_s3_w8", "dma_256x128x64_s3_w8:k2", "wstrip_16x16", "wstrip_32x16",
-         "dma_64x128x64_s4_g2", "dma_64x128x64_s4_g2:k3", "dma_256x128x32_s4", "dma_256x128x32_s4:k2"]
+         "dma_64x128x64_s4_g2", "dma_64x128x64_s4_g2:k3", "dma_256x128x64_s3", "dma_256x128x64_s3:k2"]
 # Gate/up dual-GEMM plans ("" = automatic choice); a forced DMA plan applies where K
 # is a multiple of its K step, the automatic choice elsewhere.
 DUAL_PLANS = ["", "dma_dual_256x128x32_s4", "reg_dual_256x128x64"]

@@ -130,7 +130,8 @@ def test_aliasing(L):
 
 
 def test_plans(L):
-    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4_w8"  # 256 tiles of 256^2: 8 waves
+    assert lf.plan_name(1, 4096, 4096, 4096) == "dma_256x256x32_s4"  # with RMSNorm: 4 x 1 waves
     assert lf.plan_name(0, 2048, 4096, 4096) == "dma_256x128x64_s3_w8"  # 256 tiles of 256x128: 8 waves, no split
     assert lf.plan_name(0, 2048, 4096, 11008, lf.BF16) == "dma_256x128x64_s3_w8"  # the SwiGLU down GEMM
     assert lf.plan_name(0, 1024, 4096, 4096) == "dma_128x128x64_s4_g2"  # 256 tiles of 128^2: 8-wave K-group tile
@@ -225,7 +226,7 @@ def test_workspace_bytes_sizing(L):
     MiB = 1 << 20
     lf.set_plan(None)
     # 4096^3: enough 256x256 tiles, no split
-    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4_w8"
     assert lf.workspace_bytes(0, 4096, 4096, 4096) == 0
     # 512x4096x4096 splits K two ways on 128x128 tiles: 128 tiles x 2 splits x
     # (a 128x128 fp32 tile + one sum of squares per thread and owned row block)
@@ -325,15 +326,18 @@ def test_prologue_bias_gemm_checks(L):
 
 
 def test_layernorm_and_prologue_bias_plans(L):
-    """Both prologues run in the 4 x 1 wave LDS-DMA tiles where K is a multiple
-    of 64 (256x256 while it fills the chip, then 256x128, then 128x128 with
-    split K), else in the register-staged kernel; LayerNorm keeps its row
+    """Both prologues run in the LDS-DMA tiles where K is a multiple of 64
+    (256x256 while it fills the chip, then 256x128, then 128x128 with split K:
+    4 x 1 waves for LayerNorm, the plain GEMM's 8-wave tiles for the input
+    bias), else in the register-staged kernel; LayerNorm keeps its row
     statistics (24 bytes per row) in the workspace after any split partials."""
     MiB = 1 << 20
     lf.set_plan(None)
     assert lf.plan_name(3, 4096, 4096, 4096) == "dma_256x256x32_s4"
-    assert lf.plan_name(3, 2048, 4096, 4096) == "dma_256x128x32_s4"
+    assert lf.plan_name(3, 2048, 4096, 4096) == "dma_256x128x64_s3"
     assert lf.plan_name(4, 512, 4096, 4096) == "dma_128x128x64_s4:k2"
+    assert lf.plan_name(4, 4096, 4096, 4096) == "dma_256x256x32_s4_w8"
+    assert lf.plan_name(4, 2048, 4096, 4096) == "dma_256x128x64_s3_w8"
     assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
     assert lf.plan_name(3, 4096, 4096, 4104) == "reg_256x256x64"
     assert lf.workspace_bytes(3, 4096, 4096, 4096) == MiB + 4096 * 24
@@ -348,9 +352,9 @@ def test_layernorm_and_prologue_bias_plans(L):
         assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
     finally:
         lf.set_plan(None)
-    lf.set_plan("dma_256x128x32_s4:k3")
+    lf.set_plan("dma_256x128x64_s3:k3")
     try:
-        assert lf.plan_name(3, 300, 392, 320) == "dma_256x128x32_s4:k3"
+        assert lf.plan_name(3, 300, 392, 320) == "dma_256x128x64_s3:k3"
         assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
     finally:
         lf.set_plan(None)

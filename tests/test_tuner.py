@@ -50,12 +50,12 @@ def test_candidates_follow_each_ops_constraints():
     # the gate/up pair only has the dual plans; LayerNorm and the input bias the register-staged
     # plans and the 4 x 1 wave LDS-DMA tiles
     assert all("dual" in x for x in tuner.candidates(2, 512, 1024, 1024))
-    pro_tiles = ("reg_", "dma_256x256x32_s4", "dma_256x128x32_s4", "dma_128x128x64_s4")
-    for op in (3, 4):
+    ln_tiles = ("dma_256x256x32_s4", "dma_256x128x64_s3", "dma_128x128x64_s4")
+    bias_tiles = ln_tiles + ("dma_256x256x32_s4_w8", "dma_256x128x64_s3_w8")
+    for op, tiles in ((3, ln_tiles), (4, bias_tiles)):
         c = tuner.candidates(op, 512, 1024, 1024)
-        assert all(x.split(":")[0] in ("dma_256x256x32_s4", "dma_256x128x32_s4", "dma_128x128x64_s4")
-                   or x.startswith("reg_") for x in c), c
-        assert all(any(x.startswith(t) for x in c) for t in pro_tiles), c
+        assert all(x.split(":")[0] in tiles or x.startswith("reg_") for x in c), c
+        assert all(any(x.split(":")[0] == t for x in c) for t in tiles) and any(x.startswith("reg_") for x in c), c
     # enumerating candidates leaves no entry behind
     assert lf.plan_name(1, 32, 4096, 4096) == tuner.heuristic(1, 32, 4096, 4096)
 
@@ -102,7 +102,7 @@ def test_cache_round_trip(tmp_path):
     assert tuner.read_cache(path) == data
     assert tuner.load_cache(path) == 1  # only this architecture's entries that still fit
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_64x128x64_s4_g2:k3"
-    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(0, 4096, 4096, 4096) == "dma_256x256x32_s4_w8"
     assert tuner.parse_key(tuner.cache_key(2, 2048, 11008, 4096, lf.BF16)) == (2, 2048, 11008, 4096, lf.BF16,
                                                                                "gfx950")
     with open(path, "w") as f:
