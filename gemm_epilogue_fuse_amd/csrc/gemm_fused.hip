@@ -232,8 +232,10 @@ Choice choose(const Problem& p) {
             // waves of 64x64 keep LDS reads in flight, and the taller tile
             // halves the W traffic per row of the 128x128 tile.  Measured
             // 18-20% faster than the 128x128 K-group tile at 2048x4096x4096
-            // and 2048x4096x11008.
-            pl = &kPlans[kDma256x128x64W8];
+            // and 2048x4096x11008.  With RMSNorm the 4 x 1 wave tile, which
+            // scales each A row in one wave (cold 2048x4096x4096: 84.0 us
+            // against 88.8 us).
+            pl = &kPlans[p.op == Op::RmsGemm ? kDma256x128S3 : kDma256x128x64W8];
         } else if (p.K % 64 == 0) {
             // The 8-wave tile: its second K group keeps twice the LDS reads
             // in flight and halves each wave's share of the RMS scaling.

@@ -134,6 +134,7 @@ def test_plans(L):
     assert lf.plan_name(1, 4096, 4096, 4096) == "dma_256x256x32_s4"  # with RMSNorm: 4 x 1 waves
     assert lf.plan_name(0, 2048, 4096, 4096) == "dma_256x128x64_s3_w8"  # 256 tiles of 256x128: 8 waves, no split
     assert lf.plan_name(0, 2048, 4096, 11008, lf.BF16) == "dma_256x128x64_s3_w8"  # the SwiGLU down GEMM
+    assert lf.plan_name(1, 2048, 4096, 4096) == "dma_256x128x64_s3"  # with RMSNorm: 4 x 1 waves
     assert lf.plan_name(0, 1024, 4096, 4096) == "dma_128x128x64_s4_g2"  # 256 tiles of 128^2: 8-wave K-group tile
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
     assert lf.plan_name(1, 1, 1024, 1024) == "wstrip_16x16"     # decode, a few rows, short K: column strips over all of K
