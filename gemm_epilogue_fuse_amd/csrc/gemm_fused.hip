@@ -89,8 +89,8 @@ std::atomic<int> g_override_splits{0};  // forced split count with a forced plan
 
 // The LayerNorm and input-bias prologues run in the register-staged kernel
 // and in the LDS-DMA tiles with 4 x 1 waves (each A row transformed by one
-// wave): 256x256, 256x128 and 128x128.  The input bias, one packed add per
-// pair of fp16 values, also runs in the 8-wave 256x256 and 256x128 tiles.
+// wave): 256x256, 256x128 and 128x128.  The input bias also runs in the
+// 8-wave 256x256 and 256x128 tiles (forced or tuned plans).
 bool ln_or_bias(const Problem& p) { return p.op == Op::LnGemm || p.op == Op::BiasGemm; }
 
 bool pro_plan(int idx, const Problem& p) {
@@ -194,11 +194,9 @@ Choice choose(const Problem& p) {
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
         const int64_t t256x128 = ((p.M + 255) / 256) * ((p.N + 127) / 128);
         if (p.K % 64 != 0) return {(t256 >= 224) ? &kPlans[kReg256] : &kPlans[kReg128], 1};
-        if (p.op == Op::BiasGemm)
-            // the plain GEMM's 8-wave tiles (cold 4096^3: 256x256 with 8 waves ahead of 4 x 1 waves)
-            pl = (t256 >= 224) ? &kPlans[kDma256W8] : (t256x128 >= 224) ? &kPlans[kDma256x128x64W8] : &kPlans[kDma128];
-        else
-            pl = (t256 >= 224) ? &kPlans[kDma256] : (t256x128 >= 224) ? &kPlans[kDma256x128S3] : &kPlans[kDma128];
+        // (cold 4096^3 input-bias GEMM: 126.6 us on 4 x 1 waves against 130.6 us
+        // on the 8-wave tile in fp16, 136.3 against 177.1 us in bf16)
+        pl = (t256 >= 224) ? &kPlans[kDma256] : (t256x128 >= 224) ? &kPlans[kDma256x128S3] : &kPlans[kDma128];
         return {pl, auto_splits(*pl, p)};
     }
     if (p.op != Op::RmsSwiglu && p.M <= 128 && p.K <= 1024 && plan_fits(kPlans[kWStrip16], p)) {
@@ -236,6 +234,12 @@ Choice choose(const Problem& p) {
             // scales each A row in one wave (cold 2048x4096x4096: 84.0 us
             // against 88.8 us).
             pl = &kPlans[p.op == Op::RmsGemm ? kDma256x128S3 : kDma256x128x64W8];
+        } else if (p.op == Op::RmsGemm && p.bf16 && t256x128 >= 112 && p.K % 64 == 0) {
+            // bf16 RMSNorm, whose gamma scaling costs the most VALU: the 4 x 1
+            // wave 256x128 tile with K split in two (cold 1024x4096x4096:
+            // 55.7 us against 61.4 us for the 8-wave 128x128 tile; in fp16
+            // the 128x128 tile stays ahead, 51.4 against 53.1 us)
+            pl = &kPlans[kDma256x128S3];
         } else if (p.K % 64 == 0) {
             // The 8-wave tile: its second K group keeps twice the LDS reads
             // in flight and halves each wave's share of the RMS scaling.

@@ -177,13 +177,14 @@ __device__ __forceinline__ bf16x2 bf16_pair() {
     return __builtin_bit_cast(bf16x2, r);
 }
 
-// Input-bias prologue: x + b for one 8-value A fragment, rounded once to the
-// 16-bit type (fp16: one packed add; bf16: the sum in fp32, then rounded).
+// Input-bias prologue: x + b for dwords q0..q0+nq-1 of one 8-value A
+// fragment, in place, rounded once to the 16-bit type (fp16: one packed add;
+// bf16: the sum in fp32, then rounded).
 template <bool BF>
-__device__ __forceinline__ u32x4 bias_add(u32x4 x, u32x4 b) {
-    u32x4 o;
+__device__ __forceinline__ void bias_add(u32x4& x, const u32x4& b, int q0 = 0, int nq = 4) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+        if (q < q0 || q >= q0 + nq) continue;
         const uint32_t xq = x[q];
         const uint32_t bq = b[q];
         if constexpr (BF) {
@@ -192,12 +193,11 @@ __device__ __forceinline__ u32x4 bias_add(u32x4 x, u32x4 b) {
                                                              __uint_as_float(bq << 16), false);
             const float hi = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneHi>(),
                                                              __uint_as_float(bq & 0xffff0000u), false);
-            o[q] = pack2<true>(lo, hi);
+            x[q] = pack2<true>(lo, hi);
         } else {
-            o[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xq) + __builtin_bit_cast(f16x2, bq));
+            x[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, xq) + __builtin_bit_cast(f16x2, bq));
         }
     }
-    return o;
 }
 
 // LayerNorm prologue.  The statistics pass stores per row a 16-byte record:
@@ -210,21 +210,22 @@ __device__ __forceinline__ u32x4 bias_add(u32x4 x, u32x4 b) {
 // is the GEMM of the normalised activation (x - mu) * rstd * gamma + beta.
 // Subtracting the mean before any rounding keeps rows whose mean is large
 // against their spread exact; fp16 does it in packed fp16 (mu_hi, then mu_lo,
-// then one fused multiply-add), bf16 in fp32.
+// then one fused multiply-add), bf16 in fp32.  Dwords q0..q0+nq-1, in place.
 template <bool BF>
-__device__ __forceinline__ u32x4 ln_apply(u32x4 x, u32x4 g, u32x4 be, u32x4 st) {
-    u32x4 o;
+__device__ __forceinline__ void ln_apply(u32x4& x, const u32x4& g, const u32x4& be, const u32x4& st, int q0 = 0,
+                                         int nq = 4) {
     if constexpr (BF) {
         const float mu = __uint_as_float(st[0]), sd = __uint_as_float(st[2]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            if (q < q0 || q >= q0 + nq) continue;
             const uint32_t xq = x[q], gq = g[q], bq = be[q];
             const bf16x2 xv = __builtin_bit_cast(bf16x2, xq);
             const float dlo = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneLo>(), -mu, false);
             const float dhi = __builtin_amdgcn_fdot2_f32_bf16(xv, bf16_pair<kBf16OneHi>(), -mu, false);
             const float lo = __builtin_fmaf(dlo, __uint_as_float(gq << 16), __uint_as_float(bq << 16) * sd);
             const float hi = __builtin_fmaf(dhi, __uint_as_float(gq & 0xffff0000u), __uint_as_float(bq & 0xffff0000u) * sd);
-            o[q] = pack2<true>(lo, hi);
+            x[q] = pack2<true>(lo, hi);
         }
     } else {
         const uint32_t w0 = st[0], w1 = st[1], w2 = st[2];
@@ -232,13 +233,13 @@ __device__ __forceinline__ u32x4 ln_apply(u32x4 x, u32x4 g, u32x4 be, u32x4 st) 
         const f16x2 sd = __builtin_bit_cast(f16x2, w2);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            if (q < q0 || q >= q0 + nq) continue;
             const uint32_t xq = x[q], gq = g[q], bq = be[q];
             const f16x2 d = (__builtin_bit_cast(f16x2, xq) - mh) - ml;
             const f16x2 bs = __builtin_bit_cast(f16x2, bq) * sd;
-            o[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(d, __builtin_bit_cast(f16x2, gq), bs));
+            x[q] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(d, __builtin_bit_cast(f16x2, gq), bs));
         }
     }
-    return o;
 }
 
 // The workgroup is KG groups of WM x WN waves.  Group g computes the whole
@@ -415,17 +416,26 @@ gemm_dma_kernel(const KArgs p) {
     // With sub-step read-ahead and enough matrix-core slots per sub-step,
     // the next sub-step's A blocks and gamma are read first and scaled a
     // few slots later, while this sub-step's matrix-core work runs, so no
-    // matrix-core instruction waits on the scaling.  AHEAD_SLOT is the slot
-    // that scales them (the bias and LayerNorm prologues take the last slot
-    // when a sub-step has too few, once every A and vector read is issued).
-    constexpr int AHEAD_SLOT = RMS ? FM + G0 + 2 : (FM + G0 + 2 < NMMA ? FM + G0 + 2 : NMMA - 1);
-    constexpr bool AHEAD = PV && !SRA && AHEAD_SLOT < NMMA && AHEAD_SLOT >= FM + G0;
-    // The prologue of A block i of a fragment set (bias, LayerNorm; RMS keeps its own forms).
-    auto pro_apply = [&](u32x4 a, const Frags& f, int h, int i) -> u32x4 {
-        if constexpr (PRO == kProBias) return bias_add<BF>(a, f.g[h]);
-        else if constexpr (LN) return ln_apply<BF>(a, f.g[h], f.be[h], lnst[i]);
-        else return rms_scale<BF>(a, f.g[h], ss[i]);
+    // matrix-core instruction waits on the scaling.  RMS scales them all in
+    // slot AHEAD_SLOT; the bias and LayerNorm prologues spread them (below),
+    // which needs a slot after every A and vector read is issued.
+    constexpr int AHEAD_SLOT = RMS ? FM + G0 + 2 : FM + G0;
+    constexpr bool AHEAD = PV && !SRA && AHEAD_SLOT < NMMA;
+    // Bias and LayerNorm spread their transform (below).  RMS scales all
+    // blocks in one slot: spread like the others it measured 2-7% slower.
+    constexpr bool SPREAD = AHEAD && !RMS;
+    // The prologue of dwords q0..q0+nq-1 of A block i of slot h of a
+    // fragment set (bias, LayerNorm; RMS scales whole blocks in its own forms).
+    auto pro_apply = [&](Frags& f, int h, int i, int q0 = 0, int nq = 4) {
+        if constexpr (PRO == kProBias) bias_add<BF>(f.a[h][i], f.g[h], q0, nq);
+        else if constexpr (LN) ln_apply<BF>(f.a[h][i], f.g[h], f.be[h], lnst[i], q0, nq);
+        else f.a[h][i] = rms_scale<BF>(f.a[h][i], f.g[h], ss[i]);
     };
+    // Bias and LayerNorm with sub-step read-ahead: the next sub-step's A
+    // blocks are transformed in half blocks (two dwords) spread over the slots
+    // from AHEAD_SLOT to the end of the sub-step, so no burst of VALU work
+    // holds up the next matrix-core instruction (the wave issues in order).
+    constexpr int PSLOT0 = AHEAD_SLOT, PSPAN = NMMA - PSLOT0;
     auto read_piece = [&](Frags& f, int s, int ls, int h, int r) {
         const int ks = g * KSG + ls;
         const int sbase = s * STAGE;
@@ -462,7 +472,7 @@ gemm_dma_kernel(const KArgs p) {
     auto mma = [&](Frags& cur, int h, int m) {
         const int o = m / (FM * FN), i = (m / FN) % FM, j = m % FN;
         if constexpr (PV && !SRA && !AHEAD)
-            if (o == 0 && j == 0) cur.a[h][i] = pro_apply(cur.a[h][i], cur, h, i);
+            if (o == 0 && j == 0) pro_apply(cur, h, i);
         acc[o][i][j] = mfma32<BF>(cur.a[h][i], cur.b[h][o][j], acc[o][i][j]);
     };
 
@@ -573,7 +583,7 @@ gemm_dma_kernel(const KArgs p) {
         for (int r = 0; r < NREAD; ++r) read_piece(F0, 0, 0, 0, r);
         if constexpr (AHEAD) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) F0.a[0][i] = pro_apply(F0.a[0][i], F0, 0, i);
+            for (int i = 0; i < FM; ++i) pro_apply(F0, 0, i);
         }
         // scratch of the bf16 one-slot-ahead scaling, live across the loop
         float sct[8];
@@ -612,7 +622,12 @@ gemm_dma_kernel(const KArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (do_read)
                     if (m < NREAD) read_piece(nxt, rs_stage, rs_ls, 0, m);
-                if constexpr (AHEAD && do_read)
+                if constexpr (SPREAD && do_read) {
+#pragma unroll
+                    for (int pp = 0; pp < 2 * FM; ++pp)
+                        if (m == PSLOT0 + (pp * PSPAN) / (2 * FM)) pro_apply(nxt, 0, pp >> 1, 2 * (pp & 1), 2);
+                }
+                if constexpr (AHEAD && !SPREAD && do_read)
                     if (m == AHEAD_SLOT) {
                         // all blocks in one slot: independent chains the
                         // scheduler can interleave
@@ -627,7 +642,7 @@ gemm_dma_kernel(const KArgs p) {
                             for (int i = 0; i < FM; ++i) rms_scale_bf16_ahead(nxt.a[0][i], gl, gh, ss[i], sct);
                         } else {
 #pragma unroll
-                            for (int i = 0; i < FM; ++i) nxt.a[0][i] = pro_apply(nxt.a[0][i], nxt, 0, i);
+                            for (int i = 0; i < FM; ++i) pro_apply(nxt, 0, i);
                         }
                     }
                 if constexpr (do_dma) {

@@ -135,6 +135,8 @@ def test_plans(L):
     assert lf.plan_name(0, 2048, 4096, 4096) == "dma_256x128x64_s3_w8"  # 256 tiles of 256x128: 8 waves, no split
     assert lf.plan_name(0, 2048, 4096, 11008, lf.BF16) == "dma_256x128x64_s3_w8"  # the SwiGLU down GEMM
     assert lf.plan_name(1, 2048, 4096, 4096) == "dma_256x128x64_s3"  # with RMSNorm: 4 x 1 waves
+    assert lf.plan_name(1, 1024, 4096, 4096, lf.BF16) == "dma_256x128x64_s3:k2"  # bf16 RMSNorm, 128 tiles
+    assert lf.plan_name(1, 1024, 4096, 4096) == "dma_128x128x64_s4_g2"  # fp16 keeps the K-group tile
     assert lf.plan_name(0, 1024, 4096, 4096) == "dma_128x128x64_s4_g2"  # 256 tiles of 128^2: 8-wave K-group tile
     assert lf.plan_name(1, 512, 4096, 4096) == "dma_128x128x64_s4_g2:k2"   # 128 tiles: split K in two
     assert lf.plan_name(1, 1, 1024, 1024) == "wstrip_16x16"     # decode, a few rows, short K: column strips over all of K
@@ -327,18 +329,18 @@ def test_prologue_bias_gemm_checks(L):
 
 
 def test_layernorm_and_prologue_bias_plans(L):
-    """Both prologues run in the LDS-DMA tiles where K is a multiple of 64
-    (256x256 while it fills the chip, then 256x128, then 128x128 with split K:
-    4 x 1 waves for LayerNorm, the plain GEMM's 8-wave tiles for the input
-    bias), else in the register-staged kernel; LayerNorm keeps its row
-    statistics (24 bytes per row) in the workspace after any split partials."""
+    """Both prologues run in the 4 x 1 wave LDS-DMA tiles where K is a
+    multiple of 64 (256x256 while it fills the chip, then 256x128, then
+    128x128 with split K), else in the register-staged kernel; LayerNorm keeps
+    its row statistics (24 bytes per row) in the workspace after any split
+    partials."""
     MiB = 1 << 20
     lf.set_plan(None)
     assert lf.plan_name(3, 4096, 4096, 4096) == "dma_256x256x32_s4"
     assert lf.plan_name(3, 2048, 4096, 4096) == "dma_256x128x64_s3"
     assert lf.plan_name(4, 512, 4096, 4096) == "dma_128x128x64_s4:k2"
-    assert lf.plan_name(4, 4096, 4096, 4096) == "dma_256x256x32_s4_w8"
-    assert lf.plan_name(4, 2048, 4096, 4096) == "dma_256x128x64_s3_w8"
+    assert lf.plan_name(4, 4096, 4096, 4096) == "dma_256x256x32_s4"
+    assert lf.plan_name(4, 2048, 4096, 4096) == "dma_256x128x64_s3"
     assert lf.plan_name(4, 300, 392, 328) == "reg_128x128x64"
     assert lf.plan_name(3, 4096, 4096, 4104) == "reg_256x256x64"
     assert lf.workspace_bytes(3, 4096, 4096, 4096) == MiB + 4096 * 24
