@@ -595,8 +595,15 @@ def main():
         "baseline_context": "0.208 ms fused on an NVIDIA A30 (page figure, other hardware); "
                             "vs_baseline = 0.208 ms / ms_per_step",
     }
-    del calls, sets
-    log("headline: %.3f us per call (events), %.3f us (wall)" % (dev_ms * 1e3, wall_ms * 1e3))
+    # the same work unfused through torch, over the same input sets, after the timed region
+    ucalls = [hw.unfused(s) for s in sets]
+    _, udev = time_graph(lambda i, st: ucalls[i](st), len(sets), max(40, len(sets)), 5, settle_s=0.02, replays=2)
+    rec["unfused_latency_us"] = round(udev * 1e3, 3)
+    rec["unfused"] = "torch: rms_norm, then matmul (hipBLASLt)"
+    rec["speedup_vs_unfused"] = round(udev / dev_ms, 3)
+    del calls, ucalls, sets
+    log("headline: %.3f us per call (events), %.3f us (wall); unfused torch %.3f us" %
+        (dev_ms * 1e3, wall_ms * 1e3, udev * 1e3))
 
     # ---- every other workload, fused and unfused
     if not args.no_sweep:

@@ -28,9 +28,9 @@
  *      LayerNorm(X)[m,k] = (X[m,k] - mu[m]) / sqrt(var[m] + eps) * gamma[k]
  *      + beta[k], mu and var the mean and the biased (centred) variance of
  *      row m.  Two kernels: the row statistics (written to the library
- *      workspace, 8 bytes per row), then the GEMM, whose prologue normalises
- *      each X element on its way to the matrix cores; the normalised
- *      activation is never written to memory.
+ *      workspace, 24 bytes per row), then the GEMM, whose prologue
+ *      normalises each X element on its way to the matrix cores; the
+ *      normalised activation is never written to memory.
  *
  *  fuse_gemm_prologue_bias
  *      Y = act((A + abias) . W + bias) + residual, abias [K] added to every row
@@ -56,10 +56,21 @@
  *              bias, residual, gamma) and, by default, of the output.  OR-ing
  *              FUSE_OUT_F32 makes the output float32 instead.  Products are
  *              accumulated in float32; bias, activation, residual and the
- *              RMSNorm factor are applied in float32; the output is rounded
- *              once, to nearest even.  In fuse_rmsnorm_gemm the normalised
- *              operand is rounded to the input dtype before the matrix-core
- *              multiply.
+ *              normalisation's per-row factor are applied in float32; the
+ *              output is rounded once, to nearest even.  With a prologue the
+ *              matrix-core operand is rounded once to the input dtype:
+ *              RMSNorm round(x * gamma), its row factor 1/sqrt(ms + eps)
+ *              applied to the float32 accumulator; LayerNorm round((x - mu) *
+ *              gamma + beta * s) with s = sqrt(var + eps) and 1/s applied to
+ *              the accumulator (the register-staged tiles round the
+ *              normalised value itself); input bias round(x + b).  A tile
+ *              whose rows fall outside the range where these operands keep
+ *              their precision (RMSNorm: mean square + eps below 2^-30 for
+ *              fp16 or 2^-120 for bf16, or mean square above 2^100;
+ *              LayerNorm: var + eps below 2^-24 or s at the fp16 maximum for
+ *              fp16, outside [2^-120, 2^100] for bf16), or whose accumulators came out
+ *              non-finite, is recomputed exactly: float64 row factors,
+ *              float32 operands and float32 accumulation.
  *  Shapes      M >= 0 (M == 0 is a no-op returning FUSE_OK), N >= 8, K >= 8,
  *              N % 8 == 0, K % 8 == 0; every tensor below 2^29 elements.
  *  Alignment   Every pointer 16-byte aligned.
@@ -163,9 +174,9 @@ int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
  * Y[M,N] = act(LayerNorm_{gamma,beta,eps}(X)[M,K] . W[K,N] + bias[N])
  *
  * X, gamma, W, Y required (X and Y may be NULL when M == 0); beta and bias may
- * be NULL (zero).  The normalised value is formed in float32 from fp64 row
- * statistics and rounded once to the input dtype as the matrix-core operand.
- * Uses the split-K workspace of the stream for the statistics (M * 8 bytes).
+ * be NULL (zero).  The row statistics come from a first kernel in float64 and
+ * go to the stream's workspace (M * 24 bytes, after any split-K partials);
+ * the operand is formed as described under dtype above.
  */
 int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta,
                         float eps, const void* W, const void* bias, void* Y,
@@ -176,9 +187,9 @@ int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta,
  * Y[M,N] = act((A[M,K] + abias[K]) . W[K,N] + bias[N]) + residual[M,N]
  *
  * A, abias, W, Y required (A, Y and residual may be NULL when M == 0); bias
- * and residual may be NULL.  A + abias is formed in float32 and rounded once
- * to the input dtype as the matrix-core operand.  Aliasing as for
- * fuse_gemm_epilogue.
+ * and residual may be NULL.  A + abias is rounded once to the input dtype as
+ * the matrix-core operand (fp16: one packed fp16 add; bf16: the sum in
+ * float32, then rounded).  Aliasing as for fuse_gemm_epilogue.
  */
 int fuse_gemm_prologue_bias(const void* A, const void* abias, const void* W,
                             const void* bias, const void* residual, void* Y,

@@ -246,7 +246,7 @@ def test_workspace_bytes_sizing(L):
         lf.workspace_bytes(0, 64, 12, 64)
     with pytest.raises(ValueError):
         lf.workspace_bytes(5, 64, 64, 64)
-    for op in (0, 1, 2):
+    for op in (0, 1, 2, 3, 4):
         for M in (1, 17, 32, 33, 128, 129, 512, 1024, 2048, 4096):
             for N, K in ((1024, 1024), (4096, 4096), (11008, 4096), (4096, 11008), (2048, 8192)):
                 assert lf.workspace_bytes(op, M, N, K) <= 64 * MiB, (op, M, N, K)
