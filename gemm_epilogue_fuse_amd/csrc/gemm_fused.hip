@@ -294,7 +294,8 @@ hipError_t zero_words(unsigned* p, size_t bytes, hipStream_t stream) {
 
 // LayerNorm row statistics ("llm-fusion-compiler" pattern table:
 // layernorm_gemm, the statistics pass of a two-kernel LayerNorm + GEMM): one
-// wave per row, mean and centred variance in fp64 over two passes of the row.
+// wave per row, mean and centred variance over two passes of the row, each
+// accumulated in float64 from float32 sums of 8 values.
 // Two forms per row:
 //   rec[m]  16 bytes for the LDS-DMA kernel, which forms
 //           (x - mean) * gamma + beta * s in the input type (s = sqrt(var +
@@ -327,27 +328,42 @@ __global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M,
         }
     };
     const bool held = K <= 512 * R;
+    // Sums of 8 values in float32, pairwise, then float64 across chunks and
+    // lanes: a chunk sum is off by at most 3 roundings of 2^-24 of its
+    // magnitude, far below what the fp16/bf16 operand keeps.
+    auto chunk_sum = [&](const dev::u32x4& w) {
+        float e[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            e[2 * q] = dev::lo_f32<BF>(w[q]);
+            e[2 * q + 1] = dev::hi_f32<BF>(w[q]);
+        }
+        return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    };
     double s = 0.0;
     for (int base = 0; base < K; base += 512 * R) {
         load(base);
 #pragma unroll
-        for (int c = 0; c < R; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s += (double)dev::lo_f32<BF>(v[c][q]) + (double)dev::hi_f32<BF>(v[c][q]);
+        for (int c = 0; c < R; ++c) s += (double)chunk_sum(v[c]);
     }
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     const double mu = s / (double)K;
+    // Squares about the float32 mean: sum (x - mu_f)^2 = sum (x - mu)^2 +
+    // K (mu - mu_f)^2, and (mu - mu_f)^2 is at most 2^-48 mu^2.
+    const float muf = (float)mu;
     double v2 = 0.0;
     for (int base = 0; base < K; base += 512 * R) {
         if (!held) load(base);
 #pragma unroll
         for (int c = 0; c < R; ++c) {
             if (base + 8 * (lane + 64 * c) >= K) continue;
+            float q2[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const double d0 = (double)dev::lo_f32<BF>(v[c][q]) - mu, d1 = (double)dev::hi_f32<BF>(v[c][q]) - mu;
-                v2 = fma(d0, d0, fma(d1, d1, v2));
+                const float d0 = dev::lo_f32<BF>(v[c][q]) - muf, d1 = dev::hi_f32<BF>(v[c][q]) - muf;
+                q2[q] = __builtin_fmaf(d0, d0, d1 * d1);
             }
+            v2 += (double)((q2[0] + q2[1]) + (q2[2] + q2[3]));
         }
     }
     for (int o = 32; o > 0; o >>= 1) v2 += __shfl_xor(v2, o);

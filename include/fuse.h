@@ -174,8 +174,9 @@ int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
  * Y[M,N] = act(LayerNorm_{gamma,beta,eps}(X)[M,K] . W[K,N] + bias[N])
  *
  * X, gamma, W, Y required (X and Y may be NULL when M == 0); beta and bias may
- * be NULL (zero).  The row statistics come from a first kernel in float64 and
- * go to the stream's workspace (M * 24 bytes, after any split-K partials);
+ * be NULL (zero).  The row statistics come from a first kernel (float64
+ * accumulation of float32 sums of 8 values) and go to the stream's workspace
+ * (M * 24 bytes, after any split-K partials);
  * the operand is formed as described under dtype above.
  */
 int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta,
