@@ -16,19 +16,20 @@ namespace {
 template <bool BF, bool RMS>
 const void* wide(const KernelSel& s) {
     using namespace dev;
+    constexpr int PRO = RMS ? kProRms : kProNone;
     switch (s.plan) {
     case kDma256x128W8:
-        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 6, 4, 2, 1, true, BF, RMS, 1, true>)
-                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 6, 4, 2, 1, true, BF, RMS, 1, false>);
+        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 6, 4, 2, 1, true, BF, PRO, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 6, 4, 2, 1, true, BF, PRO, 1, false>);
     case kDma256x128x64W8:
-        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, RMS, 1, true>)
-                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, RMS, 1, false>);
+        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, PRO, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 64, 3, 4, 2, 1, false, BF, PRO, 1, false>);
     case kDma64x128G2:
-        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, RMS, 1, true>)
-                       : reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, RMS, 1, false>);
+        return s.split ? reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, PRO, 1, true>)
+                       : reinterpret_cast<const void*>(&gemm_dma_kernel<64, 128, 64, 4, 1, 2, 2, true, BF, PRO, 1, false>);
     case kDual:
         if constexpr (RMS)
-            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 4, 4, 1, 1, false, BF, true, 2, false>);
+            return reinterpret_cast<const void*>(&gemm_dma_kernel<256, 128, 32, 4, 4, 1, 1, false, BF, kProRms, 2, false>);
         return nullptr;
     default:
         return nullptr;

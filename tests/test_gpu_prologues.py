@@ -204,15 +204,22 @@ def test_prologue_bias_worked_example_and_overflow(pro_plan):
     assert_close(got, want, "x + b past the fp16 maximum")
 
 
-def test_prologue_bias_full_size():
-    """4096^3 GEMM + bias + GeLU with an input bias, the automatic plan, whole output."""
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_prologue_bias_full_size(dtype):
+    """4096^3 GEMM + bias + GeLU with an input bias, the automatic plan, whole
+    output (fp16 output for fp16, float32 output for bf16)."""
     import torch
     M = N = K = 4096
-    say("prologue-bias full size", lf.plan_name(4, M, N, K))
-    d = pb_inputs(M, K, N, synth.F16, seed=99)
-    t = {k: dev_t(v, synth.F16) for k, v in d.items()}
-    x = {k: synth.widen(v, synth.F16) for k, v in d.items()}
+    code = lf.BF16 if dtype == synth.BF16 else lf.F16
+    say("prologue-bias full size", dtype, lf.plan_name(4, M, N, K, code))
+    d = pb_inputs(M, K, N, dtype, seed=99)
+    t = {k: dev_t(v, dtype) for k, v in d.items()}
+    x = {k: synth.widen(v, dtype) for k, v in d.items()}
     want = oracle.prologue_bias_gemm(x["A"], x["abias"], x["W"], x["bias"], None, "gelu_tanh")
-    got = to64(lf.gemm_prologue_bias(t["A"], t["abias"], t["W"], t["bias"], None, "gelu_tanh",
-                                     out=nan_out((M, N), torch.float16)))
+    if dtype == synth.F16:
+        got = to64(lf.gemm_prologue_bias(t["A"], t["abias"], t["W"], t["bias"], None, "gelu_tanh",
+                                         out=nan_out((M, N), torch.float16)))
+    else:
+        got = to64(lf.gemm_prologue_bias(t["A"], t["abias"], t["W"], t["bias"], None, "gelu_tanh",
+                                         out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
     assert_close(got, want, "whole output")
