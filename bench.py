@@ -530,8 +530,8 @@ def main():
     SETTLE_S = max(0.0, args.settle)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the fused kernels on a single MI355X "
-              "(no multi-GPU path); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: libfuse runs its fused kernels on a single MI355X "
+              "(there is no multi-GPU path); rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
