@@ -294,8 +294,9 @@ hipError_t zero_words(unsigned* p, size_t bytes, hipStream_t stream) {
 
 // LayerNorm row statistics ("llm-fusion-compiler" pattern table:
 // layernorm_gemm, the statistics pass of a two-kernel LayerNorm + GEMM): one
-// wave per row, mean and centred variance over two passes of the row, each
-// accumulated in float64 from float32 sums of 8 values.
+// wave per row, mean and centred variance over two passes of the row: the mean
+// from float32 sums of 8 values accumulated in float64, the variance from
+// float64 squares of the float32 differences.
 // Two forms per row:
 //   rec[m]  16 bytes for the LDS-DMA kernel, which forms
 //           (x - mean) * gamma + beta * s in the input type (s = sqrt(var +
@@ -348,8 +349,10 @@ __global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M,
     }
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     const double mu = s / (double)K;
-    // Squares about the float32 mean: sum (x - mu_f)^2 = sum (x - mu)^2 +
-    // K (mu - mu_f)^2, and (mu - mu_f)^2 is at most 2^-48 mu^2.
+    // Squares about the float32 mean, squared and summed in float64 (a float32
+    // square of a bf16 difference can leave the float32 range or fall into its
+    // subnormals): sum (x - mu_f)^2 = sum (x - mu)^2 + K (mu - mu_f)^2, and
+    // (mu - mu_f)^2 is at most 2^-48 mu^2.
     const float muf = (float)mu;
     double v2 = 0.0;
     for (int base = 0; base < K; base += 512 * R) {
@@ -357,13 +360,12 @@ __global__ void __launch_bounds__(256) ln_stats_kernel(const uint16_t* X, int M,
 #pragma unroll
         for (int c = 0; c < R; ++c) {
             if (base + 8 * (lane + 64 * c) >= K) continue;
-            float q2[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float d0 = dev::lo_f32<BF>(v[c][q]) - muf, d1 = dev::hi_f32<BF>(v[c][q]) - muf;
-                q2[q] = __builtin_fmaf(d0, d0, d1 * d1);
+                const double d0 = (double)(dev::lo_f32<BF>(v[c][q]) - muf);
+                const double d1 = (double)(dev::hi_f32<BF>(v[c][q]) - muf);
+                v2 = fma(d0, d0, fma(d1, d1, v2));
             }
-            v2 += (double)((q2[0] + q2[1]) + (q2[2] + q2[3]));
         }
     }
     for (int o = 32; o > 0; o >>= 1) v2 += __shfl_xor(v2, o);

@@ -175,8 +175,8 @@ int fuse_rmsnorm_gemm(const void* X, const void* gamma, float eps,
  *
  * X, gamma, W, Y required (X and Y may be NULL when M == 0); beta and bias may
  * be NULL (zero).  The row statistics come from a first kernel (float64
- * accumulation of float32 sums of 8 values) and go to the stream's workspace
- * (M * 24 bytes, after any split-K partials);
+ * accumulation; the mean from float32 sums of 8 values) and go to the
+ * stream's workspace (M * 24 bytes, after any split-K partials);
  * the operand is formed as described under dtype above.
  */
 int fuse_layernorm_gemm(const void* X, const void* gamma, const void* beta,

@@ -125,6 +125,32 @@ def test_layernorm_gemm_offset_and_range(pro_plan, dtype):
 
 
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+def test_layernorm_gemm_rows_outside_the_window(pro_plan, dtype):
+    """eps = 0 and rows whose variance lies outside the fast path's window
+    (fp16: rows at 2^-14 scale, var + eps below 2^-24; bf16: rows at 2^60 and
+    2^-70 scale, var outside [2^-120, 2^100]) between ordinary rows: their
+    tiles take the exact path, the others the fast one."""
+    import torch
+    M, K, N = 300, 192, 136
+    g = synth.generator(93)
+    Z = synth.normal(g, (M, K), 1.0)
+    odd = 2.0 ** -14 if dtype == synth.F16 else np.where(np.arange(M) % 2 == 0, 2.0 ** 60, 2.0 ** -70)[:, None]
+    scale = np.where((np.arange(M) % 7 == 3)[:, None], odd, 1.0)
+    X = (Z + 0.5) * scale
+    gamma = synth.normal(g, (K,), 0.1, 1.0)
+    beta = synth.normal(g, (K,), 0.1)
+    W = synth.normal(g, (K, N), 1.0 / 64.0)
+    bits = {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W))}
+    t = {k: dev_t(v, dtype) for k, v in bits.items()}
+    x = {k: synth.widen(v, dtype) for k, v in bits.items()}
+    say("ln-gemm window rows", dtype, check_plan(pro_plan, 3, M, N, K))
+    want = oracle.layernorm_gemm(x["X"], x["gamma"], 0.0, x["W"], x["beta"], None, "silu")
+    got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], 0.0, t["beta"], None, "silu",
+                                 out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+    assert_close(got, want, "rows outside the window")
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 def test_layernorm_gemm_full_size(dtype):
     """2048 x 4096 -> 4096, GeLU, the automatic plan, whole output."""
     import torch
