@@ -230,6 +230,31 @@ def test_prologue_bias_worked_example_and_overflow(pro_plan):
     assert_close(got, want, "x + b past the fp16 maximum")
 
 
+def test_prologue_bias_bf16_overflow(pro_plan):
+    """bf16: a few x + b past the bf16 maximum but inside float32's (2.5e38 +
+    9e37; their W row is scaled by 1e-38): the rounded operand is infinite, so
+    the affected tiles take the exact path (float32 operand)."""
+    import torch
+    dt = synth.BF16
+    g = synth.generator(98)
+    M, K, N = 300, 192, 136
+    A = synth.normal(g, (M, K), 1.0)
+    abias = synth.normal(g, (K,), 1.0)
+    W = synth.normal(g, (K, N), 1.0 / 64.0)
+    A[5, 3] = 2.5e38
+    A[250, 3] = 2.5e38
+    abias[3] = 9e37
+    W[3] *= 1e-38
+    bits = {k: synth.to_bits(v, dt) for k, v in (("A", A), ("ab", abias), ("W", W))}
+    t = {k: dev_t(v, dt) for k, v in bits.items()}
+    xv = {k: synth.widen(v, dt) for k, v in bits.items()}
+    say("prologue-bias bf16 overflow", check_plan(pro_plan, 4, M, N, K))
+    want = oracle.prologue_bias_gemm(xv["A"], xv["ab"], xv["W"], act_kind="gelu_tanh")
+    got = to64(lf.gemm_prologue_bias(t["A"], t["ab"], t["W"], act="gelu_tanh", out_dtype=torch.float32,
+                                     out=nan_out((M, N), torch.float32)))
+    assert_close(got, want, "x + b past the bf16 maximum")
+
+
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 def test_prologue_bias_full_size(dtype):
     """4096^3 GEMM + bias + GeLU with an input bias, the automatic plan, whole
