@@ -9,7 +9,8 @@ relu((x + bias) @ w).  Both run forced to each tile that carries them in turn
 split K, where K is a multiple of 64) over ragged shapes (including K not a
 multiple of 64 for the register-staged tiles), every activation and both
 dtypes, and at full size in the automatic plan; the whole output is compared,
-written into NaN-filled buffers.  Tolerance:
+written into NaN-filled buffers; integer data checks the plumbing of both
+prologues bit for bit.  Tolerance:
 max_abs_err <= 1.5e-2 and mean_abs_err <= 1.5e-3 (bf16 judged on a float32
 output).  Rows with a mean far from zero check that LayerNorm centres before
 it rounds; operands past the fp16 range check the tile's exact fallback.
@@ -163,6 +164,58 @@ def test_layernorm_gemm_full_size(dtype):
     got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], EPS, t["beta"], t["bias"], "gelu_tanh",
                                  out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
     assert_close(got, want, "whole output f32out")
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (7, 24, 64)])
+def test_layernorm_gemm_integer_plumbing_bit_exact(pro_plan, dtype, M, N, K):
+    """eps = 0 and rows of +-1 or +-2 with exactly zero mean (var 1 or 4, so
+    1/s = 1 or 1/2 exactly), small integer gamma, beta, W, bias: every
+    operand, product and partial sum is exact, so the whole float32 output
+    equals the oracle bit for bit on every tile (plumbing of the row records,
+    the gamma/beta slots and the row factor)."""
+    import torch
+    K = fitk(pro_plan, K)
+    K -= K % 2
+    say("ln-gemm integer plumbing", dtype, check_plan(pro_plan, 3, M, N, K), M, N, K)
+    g = synth.generator(M * 13 + K)
+    X = np.tile(np.concatenate([np.ones(K // 2), -np.ones(K // 2)]), (M, 1))
+    X = np.array([g.permutation(r) for r in X]) * np.where(np.arange(M) % 2 == 0, 1.0, 2.0)[:, None]
+    gamma = g.integers(-2, 3, K).astype(np.float64)
+    beta = g.integers(-2, 3, K).astype(np.float64)
+    W = g.integers(-1, 2, (K, N)).astype(np.float64)
+    b = g.integers(-50, 51, N).astype(np.float64)
+    bits = {k: synth.to_bits(v, dtype) for k, v in (("X", X), ("gamma", gamma), ("beta", beta), ("W", W), ("b", b))}
+    t = {k: dev_t(v, dtype) for k, v in bits.items()}
+    for act in ("none", "relu"):
+        want = oracle.layernorm_gemm(X, gamma, 0.0, W, beta, b, act)
+        got = to64(lf.layernorm_gemm(t["X"], t["gamma"], t["W"], 0.0, t["beta"], t["b"], act,
+                                     out_dtype=torch.float32, out=nan_out((M, N), torch.float32)))
+        assert np.array_equal(got, want), (act, np.abs(got - want).max())
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("M,N,K", [(300, 392, 328), (65, 136, 520), (7, 24, 64)])
+def test_prologue_bias_integer_plumbing_bit_exact(pro_plan, dtype, M, N, K):
+    """Small integer A, input bias, W, bias and residual: x + b and every
+    partial sum are exact, so the whole float32 output equals the oracle bit
+    for bit on every tile (plumbing of the bias slot against the A chunks)."""
+    import torch
+    K = fitk(pro_plan, K)
+    say("prologue-bias integer plumbing", dtype, check_plan(pro_plan, 4, M, N, K), M, N, K)
+    g = synth.generator(M * 17 + K)
+    A = g.integers(-2, 3, (M, K)).astype(np.float64)
+    ab = g.integers(-2, 3, K).astype(np.float64)
+    W = g.integers(-1, 2, (K, N)).astype(np.float64)
+    b = g.integers(-50, 51, N).astype(np.float64)
+    R = g.integers(-50, 51, (M, N)).astype(np.float64)
+    bits = {k: synth.to_bits(v, dtype) for k, v in (("A", A), ("ab", ab), ("W", W), ("b", b), ("R", R))}
+    t = {k: dev_t(v, dtype) for k, v in bits.items()}
+    for act in ("none", "relu"):
+        want = oracle.prologue_bias_gemm(A, ab, W, b, R, act)
+        got = to64(lf.gemm_prologue_bias(t["A"], t["ab"], t["W"], t["b"], t["R"], act, out_dtype=torch.float32,
+                                         out=nan_out((M, N), torch.float32)))
+        assert np.array_equal(got, want), (act, np.abs(got - want).max())
 
 
 def pb_inputs(M, K, N, dtype, seed):
